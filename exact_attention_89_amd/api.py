@@ -1,0 +1,168 @@
+"""Python binding of the C ABI in ``include/attn.h`` (argument marshalling only).
+
+Every step of attention runs in the HIP library ``libattn89.so`` that sits next
+to this file.  torch is used for device memory and streams: tensors are
+checked for device, dtype, shape and contiguity, and their pointers are passed
+through ctypes together with the current HIP stream.  There is no CPU fallback:
+if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn89.so"
+_lib = None
+
+ATTN_OK = 0
+_STATUS_NAMES = {
+    -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
+    -4: "ATTN_ERR_ALIGN", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_WORKSPACE",
+    -7: "ATTN_ERR_HIP", -8: "ATTN_ERR_TOO_LARGE",
+}
+
+# exported symbol -> (restype, argtypes); must match include/attn.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+EXPORTS = {
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "attn_materialized_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "attn_materialized": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ,
+                               _P]),
+    "attn_strerror": (ctypes.c_char_p, [_I]),
+    "attn_abi_version": (_I, []),
+}
+
+
+class AttnError(RuntimeError):
+    """A negative status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.attn_strerror(status).decode() if _lib is not None else "?"
+        super().__init__(f"{where}: {_STATUS_NAMES.get(status, status)} ({msg})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library(path: Optional[str] = None):
+    """Load (once) and return the ctypes handle of the HIP library; raise if absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()'"
+            " or python -m exact_attention_89_amd.build)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _stream_handle(torch, device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _prep(q, k, v, kv_lens, dtype):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, D]")
+    B, H, Nq, D = q.shape
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} "
+                         f"v {tuple(v.shape)}")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if kv_lens is not None:
+        if not isinstance(kv_lens, torch.Tensor):
+            kv_lens = torch.tensor(kv_lens, dtype=torch.int32, device=q.device)
+        kv_lens = kv_lens.to(device=q.device, dtype=torch.int32).contiguous()
+        if kv_lens.numel() != B:
+            raise ValueError("kv_lens must hold one length per batch entry")
+    return torch, q, k, v, kv_lens, (B, H, Nq, k.shape[2], D)
+
+
+def _call_fwd(fname, q, k, v, scale, causal, kv_lens, out, lse, dtype):
+    torch, q, k, v, kv_lens, (B, H, Nq, Nk, D) = _prep(q, k, v, kv_lens, dtype)
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != dtype or not o.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if l.shape != (B, H, Nq) or l.dtype != torch.float32 or not l.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    lib = load_library()
+    st = getattr(lib, fname)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             l.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                             kv_lens.data_ptr() if kv_lens is not None else None,
+                             _stream_handle(torch, q.device))
+    _check(st, fname)
+    return o, l
+
+
+def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_lens=None,
+             out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Fused attention forward, bf16 in/out, fp32 LSE.  Returns (o, lse)."""
+    import torch
+    return _call_fwd("attn_fwd", q, k, v, scale, causal, kv_lens, out, lse, torch.bfloat16)
+
+
+def attn_fwd_f32(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_lens=None,
+                 out=None, lse=None):
+    """Fused attention forward, fp32 in/out.  Returns (o, lse)."""
+    import torch
+    return _call_fwd("attn_fwd_f32", q, k, v, scale, causal, kv_lens, out, lse, torch.float32)
+
+
+def attn_materialized_workspace_bytes(B: int, H: int, Nq: int, Nk: int) -> int:
+    return int(load_library().attn_materialized_workspace_bytes(B, H, Nq, Nk))
+
+
+def attn_materialized(q, k, v, scale: Optional[float] = None, causal: bool = False,
+                      kv_lens=None, workspace=None, out=None, lse=None):
+    """The unfused three-launch baseline (S and P go through device memory)."""
+    torch, q, k, v, kv_lens, (B, H, Nq, Nk, D) = _prep(q, k, v, kv_lens, torch_bf16())
+    if scale is None:
+        scale = D ** -0.5
+    lib = load_library()
+    need = int(lib.attn_materialized_workspace_bytes(B, H, Nq, Nk))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib.attn_materialized(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               l.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                               kv_lens.data_ptr() if kv_lens is not None else None,
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream_handle(torch, q.device))
+    _check(st, "attn_materialized")
+    return o, l
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16

@@ -1,0 +1,125 @@
+/*
+ * attn.h -- C ABI of the exact fused attention library for MI355X (gfx950).
+ *
+ * The operation (page "Kernel Fusion and the Memory Wall", section
+ * "FlashAttention: avoid the full score matrix"):
+ *
+ *     O = softmax(Q K^T * scale + mask) V,   LSE_i = log sum_j exp(s_ij)
+ *
+ * computed in ONE kernel that keeps the score tile, the row maximum and sum,
+ * the exponentials, the online rescale by exp(m_old - m_new) and the P.V
+ * contraction on chip (page "Attention softmax fusion", sections "What fused
+ * has to mean" and "The tile loop"), so no Nq x Nk score or probability tensor
+ * is ever written to device memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer on the current HIP device.  The
+ *   caller owns and allocates every buffer; the library allocates nothing and
+ *   keeps no state between calls (it is reentrant).
+ * - Layout: contiguous row-major [B][H][N][D]; q and o use Nq rows, k and v
+ *   use Nk rows.  lse is [B][H][Nq] float32.  kv_lens is [B] int32 (device
+ *   memory) or NULL.
+ * - Mask: key j is valid for query i iff j < kv_len[b] and, when causal != 0,
+ *   j <= i (top-left aligned; also when Nq != Nk).  kv_len values outside
+ *   [0, Nk] are clamped into it; NULL means kv_len = Nk for every sequence.
+ *   kv_lens is read on the device only, never on the host.
+ * - A query row with no valid key gets O = 0 and LSE = -inf (never NaN).
+ * - LSE is the natural-log log-sum-exp of the scaled, masked scores.
+ * - scale is any finite float (typically 1/sqrt(D)).
+ * - Calls are stream-ordered: they enqueue work on `stream` (a hipStream_t;
+ *   NULL is the null stream) and return before it finishes.  A fault during
+ *   execution surfaces at the caller's next synchronisation.
+ * - On any error a negative status is returned, nothing is launched and no
+ *   output byte is written.
+ * - o and lse must not alias q, k, v or each other.
+ */
+#ifndef EXACT_ATTENTION_89_ATTN_H
+#define EXACT_ATTENTION_89_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ATTN_OK               0
+#define ATTN_ERR_NULL        -1  /* a required pointer is NULL                         */
+#define ATTN_ERR_SHAPE       -2  /* B, H, Nq or Nk < 1, or a size overflows 64 bits    */
+#define ATTN_ERR_UNSUPPORTED -3  /* head dimension D is not 64 or 128                  */
+#define ATTN_ERR_ALIGN       -4  /* q, k, v or o not 16-byte aligned, lse/kv_lens not 4 */
+#define ATTN_ERR_SCALE       -5  /* scale is NaN or infinite                           */
+#define ATTN_ERR_WORKSPACE   -6  /* workspace NULL or smaller than required            */
+#define ATTN_ERR_HIP         -7  /* the HIP runtime reported an error at launch        */
+#define ATTN_ERR_TOO_LARGE   -8  /* grid would exceed the launch limits                */
+
+/*
+ * attn_fwd -- the fused forward, bfloat16 inputs and output.
+ *
+ * q [B][H][Nq][D], k and v [B][H][Nk][D]: bfloat16 (raw 16-bit patterns).
+ * o [B][H][Nq][D]: bfloat16, written by round-to-nearest-even from the fp32
+ * result.  lse [B][H][Nq]: float32.  Products Q.K^T and P.V run on bf16
+ * matrix instructions with fp32 accumulation; P is rounded to bf16 before the
+ * P.V product, the softmax statistics stay in fp32.
+ *
+ * The whole computation is one kernel launch.  Tile loop: page "Attention
+ * softmax fusion", section "The tile loop"; online correction and deferred
+ * normalisation: page "Kernel Fusion and the Memory Wall", section
+ * "FlashAttention: avoid the full score matrix"; guard for fully masked
+ * tiles: page "Attention softmax fusion", section "Things that break".
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Nq, int Nk, int D, float scale, int causal,
+             const int32_t* kv_lens, void* stream);
+
+/*
+ * attn_fwd_f32 -- the same fused forward for float32 inputs and output.
+ * Same arguments and semantics as attn_fwd, with float32 q, k, v, o.  All
+ * arithmetic is fp32 (no rounding of P).
+ */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                 const int32_t* kv_lens, void* stream);
+
+/*
+ * attn_materialized_workspace_bytes -- bytes of workspace attn_materialized
+ * needs: the full score matrix S (float32) and the probability matrix P
+ * (bfloat16), B*H*Nq*Nk*(4 + 2) bytes plus alignment padding.  Returns 0 when
+ * a size is < 1 or the product overflows.
+ */
+size_t attn_materialized_workspace_bytes(int B, int H, int Nq, int Nk);
+
+/*
+ * attn_materialized -- the unfused three-kernel baseline, kept only to show
+ * the device-memory traffic that fusion removes (page "Fused Multi-Head
+ * Attention", the list of separate launches: score GEMM, softmax kernel,
+ * weighted-sum GEMM; page "Attention softmax fusion", section "What fused has
+ * to mean").
+ *
+ *   launch 1  S = scale * Q K^T, masked entries = -inf      -> workspace (fp32)
+ *   launch 2  P = softmax(S) row by row, LSE                -> workspace (bf16), lse
+ *   launch 3  O = P V                                        -> o
+ *
+ * Inputs, outputs and mask semantics as attn_fwd (bfloat16).  `workspace` is
+ * a caller-owned device buffer of at least
+ * attn_materialized_workspace_bytes(B, H, Nq, Nk) bytes, 256-byte aligned; its
+ * contents on return are unspecified.
+ */
+int attn_materialized(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                      const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* attn_strerror -- a static, NUL-terminated description of a status code. */
+const char* attn_strerror(int status);
+
+/* attn_abi_version -- version of this ABI (incremented on incompatible change). */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_89_ATTN_H */

@@ -1,0 +1,9 @@
+"""CPU oracle for exact attention (test infrastructure only; see attn_oracle)."""
+from .attn_oracle import (  # noqa: F401
+    attention_oracle,
+    attention_online_oracle,
+    attention_rows,
+    effective_scale,
+    kv_length,
+    valid_keys,
+)

@@ -1,0 +1,572 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each check cites where its fact comes from: a page passage, a closed form, an
+invariant of softmax, brute force on tiny inputs, or a library routine on a
+case that reduces to it.  ``PINS`` collects checks that take an attention
+implementation as an argument, so that ``test_planted_mistakes_are_caught`` can
+run them against copies of the oracle with one deliberate mistake each and show
+that every such mistake fails at least one pin.  No test here touches a GPU.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.attn_oracle as OA
+from exact_attention_89_amd.workloads import WORKLOADS, generate, random_case, round_to_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NEG_INF = -np.inf
+
+
+def _oracle(q, k, v, scale, causal=False, kv_lens=None):
+    return OA.attention_oracle(q, k, v, scale, causal=causal, kv_lens=kv_lens, row_chunk=5)
+
+
+def _rand(seed, B, H, Nq, Nk, D, Dv=None):
+    rng = np.random.default_rng(seed)
+    Dv = D if Dv is None else Dv
+    return (rng.standard_normal((B, H, Nq, D)), rng.standard_normal((B, H, Nk, D)),
+            rng.standard_normal((B, H, Nk, Dv)))
+
+
+# ---------------------------------------------------------------------------
+# brute force: softmax by its textbook definition, no max subtraction
+# ---------------------------------------------------------------------------
+
+def brute_force(q, k, v, scale, causal, kv_lens):
+    """Pure-Python loops with math.exp/math.fsum; softmax_j = e^{s_j} / sum e^{s}.
+
+    No maximum is subtracted (fine for the small scores used here), so this
+    shares neither the oracle's arithmetic order nor its stabilisation.
+    """
+    B, H, Nq, D = q.shape
+    Nk, Dv = k.shape[2], v.shape[3]
+    sigma = float(np.float32(scale))
+    o = np.zeros((B, H, Nq, Dv))
+    lse = np.full((B, H, Nq), NEG_INF)
+    for b in range(B):
+        L = Nk if kv_lens is None else min(max(int(kv_lens[b]), 0), Nk)
+        for h in range(H):
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if j < L and (not causal or j <= i)]
+                if not keys:
+                    continue
+                w = {j: math.exp(sigma * math.fsum(float(q[b, h, i, d]) * float(k[b, h, j, d])
+                                                   for d in range(D))) for j in keys}
+                z = math.fsum(w.values())
+                for e in range(Dv):
+                    o[b, h, i, e] = math.fsum(w[j] * float(v[b, h, j, e]) for j in keys) / z
+                lse[b, h, i] = math.log(z)
+    return o, lse
+
+
+def _close(a, b, tol=1e-12):
+    a, b = np.asarray(a), np.asarray(b)
+    if a.shape != b.shape:
+        return False
+    fa, fb = np.isfinite(a), np.isfinite(b)
+    if not np.array_equal(fa, fb):
+        return False
+    if not np.array_equal(a[~fa], b[~fb]):
+        return False
+    return bool(np.all(np.abs(a[fa] - b[fb]) <= tol * np.maximum(1.0, np.abs(b[fb]))))
+
+
+# ---------------------------------------------------------------------------
+# pins that take an implementation (so planted mistakes can be run through them)
+# ---------------------------------------------------------------------------
+
+def pin_brute_force(impl):
+    """Brute force on tiny shapes, every mask mode (causal x kv_len incl. 0 and > Nk)."""
+    ok = True
+    cases = [(1, 1, 5, 5, 3, False, None), (2, 2, 6, 6, 4, True, None),
+             (2, 1, 7, 9, 2, False, [3, 0]), (2, 2, 9, 9, 3, True, [4, 12]),
+             (1, 2, 4, 7, 4, True, [7]), (2, 1, 8, 3, 3, False, [-1, 2])]
+    for n, (B, H, Nq, Nk, D, causal, lens) in enumerate(cases):
+        q, k, v = _rand(100 + n, B, H, Nq, Nk, D)
+        scale = 1.0 / math.sqrt(D)
+        o, lse = impl(q, k, v, scale, causal, lens)
+        bo, blse = brute_force(q, k, v, scale, causal, lens)
+        ok &= _close(o, bo, 1e-12) and _close(lse, blse, 1e-12)
+    return ok
+
+
+def pin_two_key_closed_form(impl):
+    """Two keys with scores a and a + ln 3 give weights 1/4, 3/4; LSE = a + ln 4.
+
+    With a = 1000 the unstabilised exp overflows, so this also pins the maximum
+    subtraction of the stable softmax (page 'Kernel Fusion and the Memory Wall',
+    'Softmax needs a global row statistic').
+    """
+    ok = True
+    for a in (0.25, 1000.0, -1000.0):
+        q = np.ones((1, 1, 1, 1))
+        k = np.array([a, a + math.log(3.0)]).reshape(1, 1, 2, 1)
+        v = np.array([[2.0, -1.0], [6.0, 3.0]]).reshape(1, 1, 2, 2)
+        o, lse = impl(q, k, v, 1.0, False, None)
+        ok &= _close(o[0, 0, 0], [0.25 * 2 + 0.75 * 6, 0.25 * -1 + 0.75 * 3], 1e-12)
+        ok &= _close(lse[0, 0, 0], a + math.log(4.0), 1e-12)
+    return ok
+
+
+def pin_single_key(impl):
+    """Nk = 1: O = v_0 and LSE = s_00 = sigma * <q, k_0>."""
+    q, k, v = _rand(3, 2, 2, 4, 1, 8)
+    o, lse = impl(q, k, v, 0.3, False, None)
+    s = float(np.float32(0.3)) * np.einsum("bhid,bhjd->bhi", q, k)
+    return _close(o, np.broadcast_to(v, o.shape), 1e-12) and _close(lse, s, 1e-12)
+
+
+def pin_causal_row0(impl):
+    """Causal row 0 sees only key 0: O_0 = v_0, LSE_0 = s_00."""
+    q, k, v = _rand(4, 1, 3, 6, 6, 5)
+    o, lse = impl(q, k, v, 0.5, True, None)
+    s00 = float(np.float32(0.5)) * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0])
+    return _close(o[:, :, 0], v[:, :, 0], 1e-12) and _close(lse[:, :, 0], s00, 1e-12)
+
+
+def pin_zero_query(impl):
+    """Q = 0 (and separately scale = 0): all valid scores equal, O = mean of valid v,
+    LSE = ln(#valid)."""
+    ok = True
+    B, H, N, D = 2, 2, 7, 4
+    _, k, v = _rand(5, B, H, N, N, D)
+    lens = [5, 7]
+    for q, scale in ((np.zeros((B, H, N, D)), 0.7), (_rand(6, B, H, N, N, D)[0], 0.0)):
+        for causal in (False, True):
+            o, lse = impl(q, k, v, scale, causal, lens)
+            for b in range(B):
+                for i in range(N):
+                    nvalid = min(lens[b], i + 1) if causal else lens[b]
+                    ok &= _close(o[b, :, i], v[b, :, :nvalid].mean(axis=1), 1e-12)
+                    ok &= _close(lse[b, :, i], np.full(H, math.log(nvalid)), 1e-12)
+    return ok
+
+
+def pin_fully_masked(impl):
+    """kv_len = 0: every row has no valid key, O = 0 and LSE = -inf, no NaN
+    (page 'Attention softmax fusion', 'Things that break')."""
+    q, k, v = _rand(7, 2, 2, 5, 5, 3)
+    ok = True
+    for causal in (False, True):
+        o, lse = impl(q, k, v, 0.5, causal, [0, 3])
+        ok &= not np.isnan(o).any() and not np.isnan(lse).any()
+        ok &= bool(np.all(o[0] == 0.0)) and bool(np.all(lse[0] == NEG_INF))
+        ok &= bool(np.all(np.isfinite(lse[1])))
+    return ok
+
+
+def pin_causal_dependence(impl):
+    """Causal O_i depends on v_j, k_j only for j <= i: changing key/value i + 1 .. Nk-1
+    leaves row i unchanged, while changing key/value i changes it."""
+    q, k, v = _rand(8, 1, 1, 8, 8, 4)
+    o, _ = impl(q, k, v, 0.5, True, None)
+    ok = True
+    for i in range(7):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, i + 1:] += 3.0
+        v2[:, :, i + 1:] -= 5.0
+        o2, _ = impl(q, k2, v2, 0.5, True, None)
+        ok &= _close(o2[0, 0, i], o[0, 0, i], 1e-14)
+        v3 = v.copy()
+        v3[:, :, i] += 1.0
+        o3, _ = impl(q, k, v3, 0.5, True, None)
+        ok &= not _close(o3[0, 0, i], o[0, 0, i], 1e-6)
+    return ok
+
+
+def pin_kv_len_dependence(impl):
+    """With kv_len = L, keys L.. are ignored and key L-1 is not."""
+    q, k, v = _rand(9, 1, 1, 3, 8, 4)
+    ok = True
+    for L in (1, 4, 7):
+        o, _ = impl(q, k, v, 0.5, False, [L])
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, L:] *= -2.0
+        v2[:, :, L:] += 4.0
+        o2, _ = impl(q, k2, v2, 0.5, False, [L])
+        ok &= _close(o2, o, 1e-14)
+        v3 = v.copy()
+        v3[:, :, L - 1] += 1.0
+        o3, _ = impl(q, k, v3, 0.5, False, [L])
+        ok &= not _close(o3, o, 1e-6)
+    return ok
+
+
+def pin_shift_invariance(impl):
+    """Adding c to every score leaves O unchanged and moves LSE by c.
+
+    The shift is injected through an extra feature: q' = [q, c/sigma], k' = [k, 1].
+    """
+    q, k, v = _rand(10, 1, 2, 6, 6, 4)
+    sigma = 0.5
+    c = 7.25
+    q2 = np.concatenate([q, np.full(q.shape[:3] + (1,), c / sigma)], axis=3)
+    k2 = np.concatenate([k, np.ones(k.shape[:3] + (1,))], axis=3)
+    ok = True
+    for causal in (False, True):
+        o, lse = impl(q, k, v, sigma, causal, None)
+        o2, lse2 = impl(q2, k2, v, sigma, causal, None)
+        ok &= _close(o2, o, 1e-12) and _close(lse2, lse + c, 1e-12)
+    return ok
+
+
+def pin_key_permutation(impl):
+    """Without a causal mask, permuting (k_j, v_j) pairs jointly inside the valid prefix
+    changes nothing."""
+    q, k, v = _rand(11, 2, 1, 5, 9, 3)
+    lens = [9, 6]
+    o, lse = impl(q, k, v, 0.4, False, lens)
+    rng = np.random.default_rng(12)
+    k2, v2 = k.copy(), v.copy()
+    for b, L in enumerate(lens):
+        perm = rng.permutation(L)
+        k2[b, :, :L] = k[b][:, perm]
+        v2[b, :, :L] = v[b][:, perm]
+    o2, lse2 = impl(q, k2, v2, 0.4, False, lens)
+    return _close(o2, o, 1e-12) and _close(lse2, lse, 1e-12)
+
+
+def pin_scale_is_fp32(impl):
+    """The scale enters as an fp32 value: scale 0.1 acts as float32(0.1), and passing
+    the already-rounded value gives the identical result; 0.1 != float32(0.1)."""
+    q, k, v = _rand(13, 1, 1, 4, 4, 4)
+    q = q * 30.0
+    o1, l1 = impl(q, k, v, 0.1, False, None)
+    o2, l2 = impl(q, k, v, float(np.float32(0.1)), False, None)
+    bo, bl = brute_force(q, k, v, float(np.float32(0.1)), False, None)
+    return (np.array_equal(o1, o2) and np.array_equal(l1, l2) and _close(o1, bo, 1e-11)
+            and _close(l1, bl, 1e-11))
+
+
+def pin_dominant_key(impl):
+    """A score gap of 40 on one key: O equals that key's value to within e^-40."""
+    D = 4
+    q = np.zeros((1, 1, 1, D)); q[..., 0] = 1.0
+    k = np.zeros((1, 1, 5, D)); k[0, 0, 3, 0] = 40.0
+    v = np.arange(20, dtype=np.float64).reshape(1, 1, 5, D)
+    o, lse = impl(q, k, v, 1.0, False, None)
+    return (_close(o[0, 0, 0], v[0, 0, 3], 1e-12)
+            and abs(lse[0, 0, 0] - (40.0 + math.log1p(4 * math.exp(-40)))) < 1e-12)
+
+
+PINS = [pin_brute_force, pin_two_key_closed_form, pin_single_key, pin_causal_row0,
+        pin_zero_query, pin_fully_masked, pin_causal_dependence, pin_kv_len_dependence,
+        pin_shift_invariance, pin_key_permutation, pin_scale_is_fp32, pin_dominant_key]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    assert pin(_oracle)
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_online_oracle_pin(pin):
+    def online(q, k, v, scale, causal=False, kv_lens=None):
+        return OA.attention_online_oracle(q, k, v, scale, causal=causal, kv_lens=kv_lens, tile=3)
+    assert pin(online)
+
+
+# ---------------------------------------------------------------------------
+# the page's worked example and the online recurrence
+# ---------------------------------------------------------------------------
+
+def test_page_worked_example():
+    """Page 'Kernel Fusion and the Memory Wall', 'A small executable reference': for one
+    unmasked query, tiles of 3 over 11 keys, the online reduction equals the direct
+    softmax at rtol = atol = 1e-12."""
+    with open(os.path.join(GOLDEN, "page2_online_reduction.json")) as f:
+        g = json.load(f)
+    rng = np.random.default_rng(g["seed"])
+    q = rng.normal(size=g["d"])
+    k = rng.normal(size=(g["n_keys"], g["d"]))
+    v = rng.normal(size=(g["n_keys"], g["d_v"]))
+    scale = 1.0 / math.sqrt(g["d"])
+    # fp32(1/2) == 1/2, so the fp32 scale reading changes nothing here.
+    assert float(np.float32(scale)) == scale
+    Q, K, V = q.reshape(1, 1, 1, -1), k.reshape(1, 1, *k.shape), v.reshape(1, 1, *v.shape)
+    o_on, l_on = OA.attention_online_oracle(Q, K, V, scale, tile=g["tile"])
+    o_dir, l_dir = OA.attention_oracle(Q, K, V, scale)
+    np.testing.assert_allclose(o_on, o_dir, rtol=g["rtol"], atol=g["atol"])
+    np.testing.assert_allclose(l_on, l_dir, rtol=g["rtol"], atol=g["atol"])
+    bo, bl = brute_force(Q, K, V, scale, False, None)
+    np.testing.assert_allclose(o_dir, bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l_dir, bl, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 7, 11, 64])
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (False, [0, 5]),
+                                         (True, [13, 3])])
+def test_online_equals_direct(tile, causal, lens):
+    """Tile-by-tile recurrence with the exp(m - m') correction == direct softmax, for
+    any tile size, with masks (so some tiles are fully masked for some rows)."""
+    q, k, v = _rand(20 + tile, 2, 2, 13, 13, 5)
+    o1, l1 = OA.attention_online_oracle(q, k, v, 0.6, causal=causal, kv_lens=lens, tile=tile)
+    o2, l2 = OA.attention_oracle(q, k, v, 0.6, causal=causal, kv_lens=lens)
+    assert _close(o1, o2, 1e-12) and _close(l1, l2, 1e-12)
+
+
+def test_online_rescale_fires_with_rising_max():
+    """Keys whose scores rise tile after tile (the drifting-key recipe) make every tile
+    raise the running maximum; the recurrence must still equal the direct result."""
+    N, D = 40, 4
+    q = np.zeros((1, 1, 1, D)); q[..., 0] = 1.0
+    k = np.zeros((1, 1, N, D)); k[0, 0, :, 0] = np.arange(N) * 0.75
+    v = np.random.default_rng(3).standard_normal((1, 1, N, D))
+    o1, l1 = OA.attention_online_oracle(q, k, v, 1.0, tile=4)
+    o2, l2 = OA.attention_oracle(q, k, v, 1.0)
+    assert _close(o1, o2, 1e-12) and _close(l1, l2, 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# invariants of the result
+# ---------------------------------------------------------------------------
+
+def test_probabilities_are_a_distribution():
+    """Rows of P sum to 1, lie in [0, 1] and are 0 exactly on masked keys; the LSE is
+    self-consistent: sum_j exp(s_ij - LSE_i) = 1 over valid j."""
+    q, k, v = _rand(30, 2, 2, 9, 11, 4)
+    lens = [11, 4]
+    for causal in (False, True):
+        o, lse, p = OA.attention_oracle(q, k, v, 0.5, causal=causal, kv_lens=lens,
+                                        return_probs=True)
+        for b in range(2):
+            valid = OA.valid_keys(0, 9, 11, causal, lens[b])
+            assert np.all(p[b][:, ~valid] == 0.0)
+            assert np.all((p[b] >= 0) & (p[b] <= 1))
+            np.testing.assert_allclose(p[b].sum(-1), 1.0, rtol=0, atol=1e-12)
+            s = float(np.float32(0.5)) * np.einsum("hid,hjd->hij", q[b], k[b])
+            z = np.where(valid, np.exp(s - lse[b][..., None]), 0.0).sum(-1)
+            np.testing.assert_allclose(z, 1.0, rtol=0, atol=1e-12)
+
+
+def test_torch_sdpa_special_case():
+    """Library special case: torch's CPU scaled_dot_product_attention in float64 with a
+    boolean mask equals the oracle on rows with at least one valid key (libraries
+    differ on empty rows); LSE equals torch.logsumexp of the masked scores."""
+    torch = pytest.importorskip("torch")
+    q, k, v = _rand(31, 2, 3, 17, 17, 8)
+    lens = [17, 9]
+    scale = 1.0 / math.sqrt(8)
+    sig = float(np.float32(scale))
+    for causal in (False, True):
+        o, lse = OA.attention_oracle(q, k, v, scale, causal=causal, kv_lens=lens)
+        for b in range(2):
+            valid = torch.from_numpy(OA.valid_keys(0, 17, 17, causal, lens[b]))
+            qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x[b])) for x in (q, k, v))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qt, kt, vt, attn_mask=valid, scale=sig)
+            rows = valid.any(-1)
+            np.testing.assert_allclose(o[b][:, rows.numpy()], ref[:, rows].numpy(),
+                                       rtol=1e-12, atol=1e-12)
+            s = sig * (qt @ kt.transpose(-1, -2))
+            s = s.masked_fill(~valid, float("-inf"))
+            np.testing.assert_allclose(lse[b], torch.logsumexp(s, -1).numpy(), rtol=1e-12,
+                                       atol=1e-12)
+
+
+def test_row_chunking_changes_nothing():
+    q, k, v = _rand(32, 1, 2, 37, 37, 6)
+    a = OA.attention_oracle(q, k, v, 0.3, causal=True, kv_lens=[30], row_chunk=1024)
+    b = OA.attention_oracle(q, k, v, 0.3, causal=True, kv_lens=[30], row_chunk=4)
+    # BLAS may order its sums differently for different block sizes: agree to rounding
+    assert _close(a[0], b[0], 1e-13) and _close(a[1], b[1], 1e-13)
+
+
+def test_dv_may_differ_from_d():
+    q, k, v = _rand(33, 1, 1, 4, 6, 5, Dv=3)
+    o, lse = OA.attention_oracle(q, k, v, 0.5)
+    bo, bl = brute_force(q, k, v, 0.5, False, None)
+    assert _close(o, bo) and _close(lse, bl)
+
+
+# ---------------------------------------------------------------------------
+# the input recipe (data only; no attention arithmetic)
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_is_rne():
+    x = np.array([1.0, 1.00390625, 1.005859375, 1.0078125 + 2 ** -8, -3.14159, 65504.0,
+                  1e-40, 0.0, -0.0], dtype=np.float32)
+    r = round_to_bf16(x)
+    assert r[0] == 1.0
+    assert r[1] == 1.0                     # exactly halfway, 1.0 is even
+    assert r[2] == 1.0078125               # above half
+    assert r[3] == 1.015625                # halfway between 1.0078125 (odd) and 1.015625
+    assert r[4] == np.float32(-3.140625)
+    assert np.all(r.view(np.uint32) & 0xFFFF == 0)
+    try:
+        import torch
+        t = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(t.view(np.uint32), r.view(np.uint32))
+    except ImportError:
+        pass
+
+
+def test_workload_recipes():
+    w = WORKLOADS["bf16_padded_b8h16_n2048_d128"]
+    q, k, v, lens = generate(w, heads=1)
+    assert q.shape == (8, 1, 2048, 128) and lens.shape == (8,)
+    assert lens[0] == 0 and np.all((lens[1:] >= 1) & (lens[1:] <= 2048))
+    assert np.all(q.view(np.uint32) & 0xFFFF == 0)
+    w1 = WORKLOADS["fp32_b1h1_n128_d64"]
+    q1, _, _, l1 = generate(w1)
+    assert q1.dtype == np.float32 and l1 is None and np.any(q1.view(np.uint32) & 0xFFFF)
+    assert WORKLOADS["bf16_causal_b1h32_n8192_d128"].metric_flops() == 2.0 ** 39
+
+
+def test_drifting_keys_raise_the_max():
+    """Under the drift recipe the per-tile max score keeps rising for a query with
+    q.u > 0 (checked on a shortened draw of the same recipe)."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["bf16_causal_drift_b1h8_n32768_d128"], H=1)
+    q, k, v, _ = generate(w)
+    rng = np.random.default_rng(w.seed)
+    g = rng.standard_normal(w.D, dtype=np.float32)
+    u = g / np.linalg.norm(g.astype(np.float64))
+    qq = u.astype(np.float64) * 4.0
+    s = k[0, 0].astype(np.float64) @ qq
+    tile_max = s.reshape(-1, 1024).max(axis=1)
+    assert np.all(np.diff(tile_max) > 0)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: every one must fail at least one pin
+# ---------------------------------------------------------------------------
+
+def _mut_rows(kind):
+    orig = OA.attention_rows
+
+    def rows(q_rows, k, v, sigma, valid, return_probs=False):
+        s = sigma * (q_rows @ k.T)
+        if kind == "scale_sqrt":
+            s = math.sqrt(sigma) * (q_rows @ k.T)
+        if kind == "transposed_k":
+            s = sigma * (q_rows @ k[::-1].T)
+        s = np.where(valid, s, -np.inf)
+        m = s.max(axis=1)
+        has = m > -np.inf
+        mref = np.where(has, m, 0.0)
+        if kind == "no_max_subtraction":
+            mref = np.zeros_like(mref)
+        e = np.exp(s - mref[:, None])
+        l = e.sum(axis=1)
+        p = np.zeros_like(e)
+        p[has] = e[has] / l[has, None]
+        if kind == "no_normalisation":
+            p[has] = e[has]
+        o = p @ v
+        lse = np.full(s.shape[0], -np.inf)
+        lse[has] = (np.log(l[has]) if kind == "lse_drops_max" else m[has] + np.log(l[has]))
+        if kind == "lse_log2":
+            lse[has] = m[has] + np.log2(l[has])
+        if kind == "empty_rows_nan":
+            o[~has] = np.nan
+        else:
+            o[~has] = 0.0
+        if kind == "empty_rows_zero_lse":
+            lse[~has] = 0.0
+        return (o, lse, p) if return_probs else (o, lse)
+    return orig, rows
+
+
+def _mut_valid(kind):
+    def valid(row_lo, row_hi, nk, causal, kv_len):
+        i = np.arange(row_lo, row_hi)[:, None]
+        j = np.arange(nk)[None, :]
+        ok = (j <= kv_len) if kind == "kv_off_by_one" else (j < kv_len)
+        if causal:
+            if kind == "causal_strict":
+                ok = ok & (j < i)
+            elif kind == "causal_reversed":
+                ok = ok & (j >= i)
+            elif kind == "causal_shifted":
+                ok = ok & (j <= i + 1)
+            else:
+                ok = ok & (j <= i)
+        return ok
+    return valid
+
+
+ROW_MUTANTS = ["scale_sqrt", "transposed_k", "no_max_subtraction", "no_normalisation",
+               "lse_drops_max", "lse_log2", "empty_rows_nan",
+               "empty_rows_zero_lse"]
+MASK_MUTANTS = ["kv_off_by_one", "causal_strict", "causal_reversed", "causal_shifted"]
+
+
+def _caught(impl):
+    import warnings
+    failures = []
+    for pin in PINS:
+        try:
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                with np.errstate(all="ignore"):
+                    if not pin(impl):
+                        failures.append(pin.__name__)
+        except Exception:  # a crash is a caught mistake too
+            failures.append(pin.__name__)
+    return failures
+
+
+@pytest.mark.parametrize("kind", ROW_MUTANTS + MASK_MUTANTS)
+def test_planted_mistakes_are_caught(kind, monkeypatch):
+    if kind in ROW_MUTANTS:
+        _, rows = _mut_rows(kind)
+        monkeypatch.setattr(OA, "attention_rows", rows)
+    else:
+        monkeypatch.setattr(OA, "valid_keys", _mut_valid(kind))
+        # the brute-force reference must keep using its own mask, which it does
+    assert _caught(_oracle), f"planted mistake {kind!r} passed every pin"
+
+
+def test_unplanted_copy_passes():
+    """The mutant machinery itself, with no mistake planted, passes every pin."""
+    _, rows = _mut_rows("none")
+    orig = OA.attention_rows
+    OA.attention_rows = rows
+    try:
+        assert _caught(_oracle) == []
+    finally:
+        OA.attention_rows = orig
+
+
+def test_planted_online_mistakes_are_caught(monkeypatch):
+    """The online recurrence with the old accumulators left uncorrected (no exp(m - m'))
+    is caught by the online-vs-direct comparison once the max rises across tiles."""
+    q, k, v = _rand(40, 1, 1, 6, 12, 4)
+
+    def bad_online(q, k, v, scale, causal=False, kv_lens=None, tile=3):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        sig = float(np.float32(scale))
+        o = np.zeros(q.shape[:3] + (v.shape[3],))
+        for i in range(q.shape[2]):
+            s = sig * (k[0, 0] @ q[0, 0, i])
+            m, l, a = -np.inf, 0.0, np.zeros(v.shape[3])
+            for st in range(0, s.size, tile):
+                mn = max(m, s[st:st + tile].max())
+                e = np.exp(s[st:st + tile] - mn)
+                l = l + e.sum()               # correction dropped
+                a = a + e @ v[0, 0, st:st + tile]
+                m = mn
+            o[0, 0, i] = a / l
+        return o
+    ref, _ = OA.attention_oracle(q, k, v, 0.8)
+    assert not _close(bad_online(q, k, v, 0.8), ref, 1e-6)
+    good, _ = OA.attention_online_oracle(q, k, v, 0.8, tile=3)
+    assert _close(good, ref, 1e-12)
+
+
+def test_small_workload_through_oracle_is_finite():
+    """The smallest workload end to end: finite outputs, LSE finite everywhere."""
+    w = WORKLOADS["fp32_b1h1_n128_d64"]
+    q, k, v, lens = generate(w)
+    o, lse = OA.attention_oracle(q, k, v, w.scale, causal=w.causal, kv_lens=lens)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    bo, bl = brute_force(q[:, :, :6], k, v, w.scale, False, None)
+    assert _close(o[:, :, :6], bo, 1e-11) and _close(lse[:, :, :6], bl, 1e-11)
