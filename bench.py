@@ -1,0 +1,190 @@
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one call of attn_fwd (the whole fused forward, one kernel launch) on the
+seeded synthetic inputs of a workload, already resident in device memory.  W
+untimed steps, then exactly K timed steps between two device synchronisations.
+Prints ONE JSON line:
+
+* value / unit: attention TFLOP/s = 4*B*H*Nq*Nk*D (halved when causal) / time
+* roofline: the same algorithmic flop count divided by the kernel's mean launch
+  duration (HIP events around each launch, on the launch stream), against the
+  bf16 dense matrix peak of MI355X (2.5 PFLOP/s); ``traffic`` is the measured
+  device-memory traffic per launch from a committed rocprofv3 counter summary,
+  reported only if it was taken on the current kernel source (else null)
+* cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
+  workload on this host, in the same unit.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_89_amd", "csrc", "attn_fwd_bf16.hip")
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for fn in ("attn_fwd_bf16.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "exact_attention_89_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from profiles/traffic_<workload>.json, if current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    fused = rec.get("fused", {})
+    if fused.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return fused.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, lens, budget_s):
+    """Time the fp64 oracle on whole heads of the workload until ``budget_s`` passes."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            oracle.attention_oracle(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
+                                    v[b:b + 1, h:h + 1], w.scale, causal=w.causal,
+                                    kv_lens=None if lens is None else lens[b:b + 1])
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.metric_flops() / (w.B * w.H) * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (batch, head) pairs of {w.name}, every query "
+                      f"row, fp64 numpy oracle, {dt:.1f} s wall; flops counted as in the "
+                      f"metric"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the fused "
+              "forward shards by (batch, head) with no communication, so a multi-GPU figure "
+              "would be N independent copies of this one", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from exact_attention_89_amd import api
+    from exact_attention_89_amd.workloads import HEADLINE, WORKLOADS, generate
+
+    if not os.path.exists(api.library_path()):
+        from exact_attention_89_amd import build
+        build.build()
+    api.load_library()
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    if w.dtype != "bf16":
+        raise SystemExit("bench.py times the bf16 path")
+    log(f"[bench] generating {name}")
+    q, k, v, lens = generate(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    ld = None if lens is None else torch.from_numpy(lens).to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+
+    def step():
+        api.attn_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, kv_lens=ld, out=o, lse=lse)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    total_ms = ev[0][0].elapsed_time(ev[-1][1])
+    ms_per_step = total_ms / args.steps
+    flops = w.metric_flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    mean_launch_ms = float(np.mean(launch_ms))
+    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+    log(f"[bench] {name}: {ms_per_step:.4f} ms/step (events), wall {wall / args.steps * 1e3:.4f}"
+        f" ms/step, launch median {np.median(launch_ms):.4f} ms, p10 "
+        f"{np.percentile(launch_ms, 10):.4f}, p90 {np.percentile(launch_ms, 90):.4f}")
+    assert not torch.isnan(o).any().item(), "NaN in the output"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu_baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(w, q, k, v, lens, args.cpu_seconds)
+
+    traffic = measured_traffic(name)
+    line = {
+        "metric": "fused attn fwd TFLOP/s + % bf16 MFMA peak (B,H,N,D=1,32,8192,128 causal)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
+                   "causal": w.causal, "seed": w.seed,
+                   "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

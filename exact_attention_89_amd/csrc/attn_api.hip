@@ -1,0 +1,124 @@
+// attn_api.hip -- the C ABI of include/attn.h: argument checks, then dispatch.
+//
+// Every check runs before anything is launched, so an error status means no
+// kernel ran and no output was written.  kv_lens is device memory and is not read
+// here (that would need a synchronisation); the kernels clamp its entries.
+
+#include <math.h>
+
+#include "../../include/attn.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 int B, int H, int Nq, int Nk, int D, float scale, const int32_t* kv_lens,
+                 size_t elem_bytes) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  size_t bh = 0, nq = 0, nk = 0, bytes = 0;
+  if (__builtin_mul_overflow((size_t)B, (size_t)H, &bh)) return ATTN_ERR_SHAPE;
+  if (__builtin_mul_overflow(bh, (size_t)Nq, &nq)) return ATTN_ERR_SHAPE;
+  if (__builtin_mul_overflow(bh, (size_t)Nk, &nk)) return ATTN_ERR_SHAPE;
+  if (__builtin_mul_overflow(nq > nk ? nq : nk, (size_t)D * elem_bytes, &bytes))
+    return ATTN_ERR_SHAPE;
+  if (bh > 0x7fffffffULL) return ATTN_ERR_TOO_LARGE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return ATTN_ERR_ALIGN;
+  if (!aligned(lse, 4) || (kv_lens && !aligned(kv_lens, 4))) return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  return ATTN_OK;
+}
+
+attn89::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Nq, int Nk, float scale, int causal,
+                          const int32_t* kv_lens) {
+  attn89::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.kv_lens = kv_lens;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.causal = causal ? 1 : 0;
+  const float c = scale * attn89::kLog2e;
+  if (scale > 0.f) {
+    a.c_exp = c;
+    a.c_pre = 1.f;
+    a.pre_scale = 0;
+  } else {
+    a.c_exp = 1.f;
+    a.c_pre = c;
+    a.pre_scale = 1;
+  }
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int Nq, int Nk, int D, float scale, int causal, const int32_t* kv_lens,
+             void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, kv_lens, 2);
+  if (st != ATTN_OK) return st;
+  attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
+  return attn89::launch_attn_fwd_bf16(a, D, (hipStream_t)stream);
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                 int H, int Nq, int Nk, int D, float scale, int causal, const int32_t* kv_lens,
+                 void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, kv_lens, 4);
+  if (st != ATTN_OK) return st;
+  attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
+  return attn89::launch_attn_fwd_f32(a, D, (hipStream_t)stream);
+}
+
+size_t attn_materialized_workspace_bytes(int B, int H, int Nq, int Nk) {
+  attn89::MatLayout lay;
+  if (!attn89::materialized_layout(B, H, Nq, Nk, &lay)) return 0;
+  return lay.total;
+}
+
+int attn_materialized(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Nq, int Nk, int D, float scale, int causal,
+                      const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, kv_lens, 2);
+  if (st != ATTN_OK) return st;
+  attn89::MatLayout lay;
+  if (!attn89::materialized_layout(B, H, Nq, Nk, &lay)) return ATTN_ERR_SHAPE;
+  if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256))
+    return ATTN_ERR_WORKSPACE;
+  attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
+  return attn89::launch_attn_materialized(a, D, scale, workspace, lay, (hipStream_t)stream);
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H, Nq and Nk must be >= 1 and the sizes must fit 64 bits";
+    case ATTN_ERR_UNSUPPORTED: return "head dimension must be 64 or 128";
+    case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned; lse, kv_lens 4-byte";
+    case ATTN_ERR_SCALE: return "scale must be finite";
+    case ATTN_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case ATTN_ERR_HIP: return "the HIP runtime reported a launch error";
+    case ATTN_ERR_TOO_LARGE: return "problem exceeds the kernel launch limits";
+    default: return "unknown status";
+  }
+}
+
+int attn_abi_version(void) { return 1; }
+
+}  // extern "C"

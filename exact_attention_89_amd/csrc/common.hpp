@@ -1,0 +1,57 @@
+// common.hpp -- types and small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn89 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Arguments of the fused forward kernels (device pointers, sizes in elements).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* kv_lens;  // [B] or nullptr
+  int B, H, Nq, Nk;
+  // Scores enter the exponent as s * c_exp.  When scale > 0, c_exp = scale*log2(e)
+  // and the raw dot products are used directly; otherwise the dot products are first
+  // multiplied by c_pre = scale*log2(e) and c_exp = 1 (so that -inf masking stays
+  // correct for scale <= 0).
+  float c_exp;
+  float c_pre;
+  int pre_scale;  // 1 when c_pre must be applied
+  int causal;
+};
+
+__device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int nk) {
+  if (kv_lens == nullptr) return nk;
+  int n = kv_lens[b];
+  return n < 0 ? 0 : (n > nk ? nk : n);
+}
+
+// round-to-nearest-even float -> bf16 bits, two at a time (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (unsigned int)__builtin_bit_cast(unsigned short, a) |
+         ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
+  return __uint_as_float(((unsigned int)h) << 16);
+}
+
+}  // namespace attn89

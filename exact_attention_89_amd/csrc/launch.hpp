@@ -1,0 +1,27 @@
+// launch.hpp -- host-side launchers of the kernels (internal to the library).
+// Each returns 0, or a negative status of include/attn.h.  Arguments are validated
+// by the caller (attn_api.hip) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace attn89 {
+
+int launch_attn_fwd_bf16(const FwdArgs& a, int D, hipStream_t stream);
+int launch_attn_fwd_f32(const FwdArgs& a, int D, hipStream_t stream);
+
+// Workspace layout of the materialised baseline: S (fp32) then P (bf16), both
+// [B][H][Nq][ld] with ld = Nk rounded up to a multiple of 64.
+struct MatLayout {
+  int ld;
+  size_t s_bytes;
+  size_t p_offset;
+  size_t total;
+};
+bool materialized_layout(int B, int H, int Nq, int Nk, MatLayout* out);
+int launch_attn_materialized(const FwdArgs& a, int D, float scale, void* workspace,
+                             const MatLayout& lay, hipStream_t stream);
+
+}  // namespace attn89

@@ -2,6 +2,7 @@
 from .attn_oracle import (  # noqa: F401
     attention_oracle,
     attention_online_oracle,
+    attention_oracle_rows,
     attention_rows,
     effective_scale,
     kv_length,

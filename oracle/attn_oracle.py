@@ -70,6 +70,7 @@ __all__ = [
     "attention_oracle",
     "attention_online_oracle",
     "attention_rows",
+    "attention_oracle_rows",
 ]
 
 
@@ -222,4 +223,26 @@ def attention_online_oracle(q, k, v, scale: float, causal: bool = False, kv_lens
                 if normalizer > 0.0:
                     o[b, h, i] = numerator / normalizer
                     lse[b, h, i] = maximum + math.log(normalizer)
+    return o, lse
+
+
+def attention_oracle_rows(q, k, v, scale: float, causal: bool, kv_lens, samples):
+    """The definition evaluated on selected rows only: ``samples`` lists (b, h, i).
+
+    Returns O [n, Dv] and LSE [n] (fp64) for those rows, each computed exactly as
+    ``attention_oracle`` computes it, so large problems can be checked row by row.
+    """
+    Nk = k.shape[2]
+    sigma = effective_scale(scale)
+    samples = list(samples)
+    o = np.zeros((len(samples), v.shape[3]))
+    lse = np.full(len(samples), -np.inf)
+    for n, (b, h, i) in enumerate(samples):
+        L = kv_length(kv_lens, b, Nk)
+        valid = valid_keys(i, i + 1, Nk, causal, L)
+        res = attention_rows(np.asarray(q[b, h, i:i + 1], dtype=np.float64),
+                             np.asarray(k[b, h], dtype=np.float64),
+                             np.asarray(v[b, h], dtype=np.float64), sigma, valid)
+        o[n] = res[0][0]
+        lse[n] = res[1][0]
     return o, lse

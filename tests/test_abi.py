@@ -1,0 +1,109 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, and rejects invalid arguments before launching anything (these calls
+return from host-side checks and never touch a device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_89_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.library_path()):
+        from exact_attention_89_amd import build
+        build.build()
+    return api.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    assert names == sorted(["attn_fwd", "attn_fwd_f32", "attn_materialized",
+                            "attn_materialized_workspace_bytes", "attn_strerror",
+                            "attn_abi_version"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert name in api.EXPORTS, f"binding does not describe {name}"
+
+
+def test_status_strings(lib):
+    assert lib.attn_abi_version() == 1
+    for st in range(-8, 1):
+        assert lib.attn_strerror(st)
+    assert lib.attn_strerror(-99) == b"unknown status"
+
+
+def test_workspace_size(lib):
+    # S fp32 + P bf16 over [B][H][Nq][round_up(Nk, 64)], P starting 256-byte aligned
+    assert lib.attn_materialized_workspace_bytes(1, 32, 8192, 8192) == 32 * 8192 * 8192 * 6
+    assert lib.attn_materialized_workspace_bytes(2, 3, 5, 70) == 2 * 3 * 5 * 128 * 6 + 0
+    assert lib.attn_materialized_workspace_bytes(0, 1, 1, 1) == 0
+    assert lib.attn_materialized_workspace_bytes(1, 1, 1, -5) == 0
+
+
+A = 1 << 20  # a 16-byte aligned fake address: these calls must fail before any use
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_f32"])
+def test_invalid_arguments(lib, fn):
+    f = getattr(lib, fn)
+
+    def call(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=8, Nk=8, D=64, scale=0.125, causal=0,
+             kv=None):
+        return f(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, kv, None)
+
+    assert call(q=None) == -1
+    assert call(lse=None) == -1
+    assert call(B=0) == -2
+    assert call(Nk=-1) == -2
+    assert call(B=1 << 30, H=1 << 30, Nq=1 << 30) == -2
+    assert call(D=96) == -3
+    assert call(D=0) == -3
+    assert call(q=A + 8) == -4
+    assert call(o=A + 2) == -4
+    assert call(lse=A + 2) == -4
+    assert call(kv=A + 1) == -4
+    assert call(scale=float("nan")) == -5
+    assert call(scale=float("-inf")) == -5
+
+
+def test_materialized_invalid_arguments(lib):
+    f = lib.attn_materialized
+    need = lib.attn_materialized_workspace_bytes(1, 1, 8, 8)
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, None, None, need, None) == -6
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, None, A, need - 1, None) == -6
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, None, A + 16, need, None) == -6
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 80, 0.1, 0, None, A, need, None) == -3
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        api.attn_fwd(x, x, x)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package never imports the oracle (it is test infrastructure only)."""
+    pkg = os.path.join(ROOT, "exact_attention_89_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), fn
+                assert "attn_oracle" not in text, fn

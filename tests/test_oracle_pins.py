@@ -570,3 +570,15 @@ def test_small_workload_through_oracle_is_finite():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     bo, bl = brute_force(q[:, :, :6], k, v, w.scale, False, None)
     assert _close(o[:, :, :6], bo, 1e-11) and _close(lse[:, :, :6], bl, 1e-11)
+
+
+def test_sampled_rows_match_full_oracle():
+    """The row-by-row entry point computes the same rows as the full definition."""
+    q, k, v = _rand(41, 2, 2, 11, 13, 4)
+    lens = [13, 5]
+    for causal in (False, True):
+        o, lse = OA.attention_oracle(q, k, v, 0.5, causal=causal, kv_lens=lens)
+        samples = [(b, h, i) for b in range(2) for h in range(2) for i in (0, 3, 6, 10)]
+        so, sl = OA.attention_oracle_rows(q, k, v, 0.5, causal, lens, samples)
+        for n, (b, h, i) in enumerate(samples):
+            assert _close(so[n], o[b, h, i], 1e-13) and _close(sl[n], lse[b, h, i], 1e-13)
