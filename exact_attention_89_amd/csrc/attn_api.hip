@@ -71,6 +71,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              void* stream) {
   int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, kv_lens, 2);
   if (st != ATTN_OK) return st;
+  // one head of q or k/v (plus a tile of slack) must be addressable with 32-bit
+  // byte offsets by the kernel's buffer loads
+  if (((size_t)Nq + 256) * D * 2 >= ((size_t)1 << 31) ||
+      ((size_t)Nk + 256) * D * 2 >= ((size_t)1 << 31))
+    return ATTN_ERR_TOO_LARGE;
   attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
   return attn89::launch_attn_fwd_bf16(a, D, (hipStream_t)stream);
 }

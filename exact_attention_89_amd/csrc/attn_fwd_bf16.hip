@@ -58,6 +58,28 @@ struct Cfg {
   static constexpr int KBLK = BC / 32;     // 32-key blocks of a tile
 };
 
+// v_permlane32_swap exchanges the upper half-wave of one operand with the lower
+// half-wave of the other; with both operands = x, the two results of every lane are
+// x[l] and x[l ^ 32] (in some order), so their max / sum is the two-lane reduction.
+__device__ __forceinline__ float max_with_partner(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_with_partner(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+#ifndef ATTN89_RESCALE_SLACK
+#define ATTN89_RESCALE_SLACK 0.0f
+#endif
+// How far (log2 units) the row maximum may rise above the exponent reference
+// before the accumulators are corrected; 0 corrects on every rise.
+constexpr float kRescaleSlack = ATTN89_RESCALE_SLACK;
+
 __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
@@ -100,41 +122,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
   const int wave_end = (qw >= p.Nq) ? 0 : (p.causal ? min(L, min(qw + 32, p.Nq)) : L);
 
   // ---- Q fragments: B operand of S^T = K Q^T, resident for the whole loop ----
+  // Buffer loads: rows past Nq (or keys past kv_len below) read as zeros.
   const int qrow = qw + lq;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)p.Nq * D * 2);
   bf16x8 qf[C::DSTEPS];
 #pragma unroll
-  for (int s = 0; s < C::DSTEPS; ++s) {
-    if (qrow < p.Nq) {
-      qf[s] = *(const bf16x8*)(qp + (size_t)qrow * D + 16 * s + 8 * lg);
-    } else {
-      qf[s] = (bf16x8){};
-    }
-  }
+  for (int s = 0; s < C::DSTEPS; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, ((unsigned)qrow * D + 16 * s + 8 * lg) * 2));
 
   // ---- tile staging: global -> registers -> LDS ----
   u32x4 kreg[C::K_PER_T];
   u32x4 vreg[C::V_PER_T][4];
 
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)L * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (unsigned)L * D * 2);
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < C::K_PER_T; ++i) {
       const int c = tid + C::NT * i;
       const int row = c / (D / 8);
       const int col = (c % (D / 8)) * 8;
-      const int key = j0 + row;
-      kreg[i] = key < L ? *(const u32x4*)(kp + (size_t)key * D + col) : (u32x4){0, 0, 0, 0};
+      kreg[i] = buffer_load16(krs, ((unsigned)(j0 + row) * D + col) * 2);
     }
 #pragma unroll
     for (int i = 0; i < C::V_PER_T; ++i) {
       const int u = tid + C::NT * i;
       const int kg = u % (C::BC / 4);
       const int dg = u / (C::BC / 4);
+      if (u < C::V_UNITS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j0 + 4 * kg + r;
-        vreg[i][r] = (u < C::V_UNITS && key < L)
-                         ? *(const u32x4*)(vp + (size_t)key * D + 8 * dg)
-                         : (u32x4){0, 0, 0, 0};
+        for (int r = 0; r < 4; ++r)
+          vreg[i][r] = buffer_load16(vrs, ((unsigned)(j0 + 4 * kg + r) * D + 8 * dg) * 2);
       }
     }
   };
@@ -185,6 +203,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
     load_tile(0);
     store_tile(0);
   }
+  // Drain every outstanding global load (the Q fragments included) before the loop,
+  // so inside it the only loads in flight are the next tile's prefetch and no
+  // matrix instruction waits on them.  Encoding: vmcnt(0), expcnt and lgkmcnt
+  // unconstrained.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
@@ -195,17 +218,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
     if (j0 < wave_end) {
       const unsigned short* ks = smem + buf * C::K_ELEMS;
       const unsigned short* vt = smem + 2 * C::K_ELEMS + buf * C::V_ELEMS;
-      // S^T = K Q^T for the tile, fp32 accumulation
+      // S^T = K Q^T for the tile, fp32 accumulation.  The K fragments of the next
+      // 32-key block are read from LDS before the MFMAs of the current one are
+      // issued, so LDS latency hides behind matrix work.
       f32x16 sacc[C::KBLK];
+      bf16x8 kf[2][C::DSTEPS];
+      const unsigned short* kbase = ks + krow_perm * C::KSTR + 8 * lg;
+#pragma unroll
+      for (int s = 0; s < C::DSTEPS; ++s) kf[0][s] = *(const bf16x8*)(kbase + 16 * s);
 #pragma unroll
       for (int kb = 0; kb < C::KBLK; ++kb) {
-        sacc[kb] = (f32x16){};
-        const unsigned short* krow = ks + (kb * 32 + krow_perm) * C::KSTR + 8 * lg;
+        if (kb + 1 < C::KBLK) {
 #pragma unroll
-        for (int s = 0; s < C::DSTEPS; ++s) {
-          const bf16x8 a = *(const bf16x8*)(krow + 16 * s);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+          for (int s = 0; s < C::DSTEPS; ++s)
+            kf[(kb + 1) & 1][s] = *(const bf16x8*)(kbase + (kb + 1) * 32 * C::KSTR + 16 * s);
         }
+        sacc[kb] = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < C::DSTEPS; ++s)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][s], qf[s], sacc[kb], 0, 0, 0);
       }
       if (p.pre_scale) {
 #pragma unroll
@@ -231,9 +262,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
       for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c_exp);
-      // guard: a row with no valid key so far has m_new = -inf; use 0 as the
+      mx = max_with_partner(mx) * c_exp;
+      // Online correction.  The exponent reference m_run moves to the new maximum
+      // only when the maximum rises by more than kRescaleSlack (log2 units); until
+      // then the exponentials are taken against the older reference and stay
+      // <= 2^kRescaleSlack.  Numerator and normaliser always share one reference, so
+      // a / l is unchanged; moving the reference multiplies both by
+      // alpha = exp2(m_old - m_new), exactly the correction of the recurrence.
+      const bool move = mx > m_run + kRescaleSlack;
+      const float m_new = move ? mx : m_run;
+      // guard: a row with no valid key so far keeps m_new = -inf; use 0 as the
       // exponent reference so that no -inf - (-inf) appears
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -248,11 +286,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
           sacc[kb][r] = e;
           lsum += e;
         }
-      l_run = alpha * l_run + lsum;
+      if (__any(move)) {
+        // alpha == 1 exactly on rows whose reference did not move
+        l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < C::DBLK; ++d)
+        for (int d = 0; d < C::DBLK; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+      }
+      l_run += lsum;
 
       // P -> bf16, laid out as the B operand of O^T = V^T P^T
       bf16x8 pf[C::KBLK][2];
@@ -266,17 +308,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
             w[x] = pack_bf16x2(sacc[kb][8 * j + 2 * x], sacc[kb][8 * j + 2 * x + 1]);
           pf[kb][j] = __builtin_bit_cast(bf16x8, w);
         }
-      // O^T += V^T P^T
+      // O^T += V^T P^T, with the V^T fragments of the next 32 dimensions read ahead
+      bf16x8 vf[2][C::KBLK * 2];
+      const unsigned short* vbase = vt + lq * C::VSTR + 8 * lg;
+#pragma unroll
+      for (int x = 0; x < C::KBLK * 2; ++x) vf[0][x] = *(const bf16x8*)(vbase + 16 * x);
 #pragma unroll
       for (int d = 0; d < C::DBLK; ++d) {
-        const unsigned short* vrow = vt + (d * 32 + lq) * C::VSTR + 8 * lg;
+        if (d + 1 < C::DBLK) {
+#pragma unroll
+          for (int x = 0; x < C::KBLK * 2; ++x)
+            vf[(d + 1) & 1][x] = *(const bf16x8*)(vbase + (d + 1) * 32 * C::VSTR + 16 * x);
+        }
 #pragma unroll
         for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const bf16x8 a = *(const bf16x8*)(vrow + kb * 32 + 16 * j);
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][j], oacc[d], 0, 0, 0);
-          }
+          for (int j = 0; j < 2; ++j)
+            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[d & 1][2 * kb + j], pf[kb][j],
+                                                              oacc[d], 0, 0, 0);
       }
     }
 
@@ -285,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
   }
 
   // ---- epilogue: O = a / l (0 for rows with no valid key), LSE = ln2 (m + log2 l) ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_with_partner(l_run);
   if (qrow < p.Nq) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     unsigned short* orow = op + (size_t)qrow * D;

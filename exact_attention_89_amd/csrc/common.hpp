@@ -12,6 +12,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
@@ -42,12 +44,20 @@ __device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int nk) 
   return n < 0 ? 0 : (n > nk ? nk : n);
 }
 
-// round-to-nearest-even float -> bf16 bits, two at a time (v_cvt_pk_bf16_f32 on gfx950)
+// round-to-nearest-even float -> bf16 bits, two at a time: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (unsigned int)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2));
+}
+
+// Buffer resource over [base, base + nbytes): loads at offsets >= nbytes return 0
+// (raw buffer addressing, range checked by the hardware), so tails need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
