@@ -34,6 +34,8 @@
 // LDS rows are padded by 16 bytes so the 16-byte fragment reads of 16 lanes cover
 // all 64 banks without conflict.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -119,7 +121,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
   const int kv_end = p.causal ? min(L, q_hi) : L;    // keys any row of the block sees
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
   const int qw = q0 + wave * 32;
-  const int wave_end = (qw >= p.Nq) ? 0 : (p.causal ? min(L, min(qw + 32, p.Nq)) : L);
 
   // ---- Q fragments: B operand of S^T = K Q^T, resident for the whole loop ----
   // Buffer loads: rows past Nq (or keys past kv_len below) read as zeros.
@@ -131,12 +132,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
     qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, ((unsigned)qrow * D + 16 * s + 8 * lg) * 2));
 
   // ---- tile staging: global -> registers -> LDS ----
+  // K runs one tile ahead of V: while tile t is exponentiated and multiplied into O,
+  // the scores of tile t+1 are already being produced.  Iteration t reads K(t+1)
+  // from K buffer (t+1)&1 and V(t) from V buffer t&1, and writes K(t+2) into K
+  // buffer t&1 and V(t+1) into V buffer (t+1)&1; one barrier per iteration.
   u32x4 kreg[C::K_PER_T];
   u32x4 vreg[C::V_PER_T][4];
 
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)L * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (unsigned)L * D * 2);
-  auto load_tile = [&](int j0) {
+  auto load_k = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < C::K_PER_T; ++i) {
       const int c = tid + C::NT * i;
@@ -144,6 +149,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
       const int col = (c % (D / 8)) * 8;
       kreg[i] = buffer_load16(krs, ((unsigned)(j0 + row) * D + col) * 2);
     }
+  };
+  auto load_v = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < C::V_PER_T; ++i) {
       const int u = tid + C::NT * i;
@@ -156,10 +163,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
       }
     }
   };
-
-  auto store_tile = [&](int buf) {
+  auto store_k = [&](int buf) {
     unsigned short* ks = smem + buf * C::K_ELEMS;
-    unsigned short* vt = smem + 2 * C::K_ELEMS + buf * C::V_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::K_PER_T; ++i) {
       const int c = tid + C::NT * i;
@@ -167,6 +172,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
       const int col = (c % (D / 8)) * 8;
       *(u32x4*)(ks + row * C::KSTR + col) = kreg[i];
     }
+  };
+  auto store_v = [&](int buf) {
+    unsigned short* vt = smem + 2 * C::K_ELEMS + buf * C::V_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::V_PER_T; ++i) {
       const int u = tid + C::NT * i;
@@ -189,149 +197,159 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
     }
   };
 
+  const int krow_perm = swap_bits23(lq);
+  // S^T = K Q^T for the 64 keys held in K buffer kbuf, fp32 accumulation
+  auto qk = [&](int kbuf, f32x16* sacc) {
+    const unsigned short* kbase = smem + kbuf * C::K_ELEMS + krow_perm * C::KSTR + 8 * lg;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb) sacc[kb] = (f32x16){};
+    // consecutive matrix instructions go to different accumulators
+#pragma unroll
+    for (int s = 0; s < C::DSTEPS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < C::KBLK; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kbase + kb * 32 * C::KSTR + 16 * s);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+      }
+  };
+
   // ---- running state: one query per lane (shared by lanes l and l^32) ----
   f32x16 oacc[C::DBLK];
 #pragma unroll
   for (int d = 0; d < C::DBLK; ++d) oacc[d] = (f32x16){};
-  float m_run = kNegInf;  // running max of s*c (log2 domain)
+  float m_run = kNegInf;  // exponent reference: running max of s*c (log2 domain)
   float l_run = 0.f;      // this lane's part of the running sum
-
   const float c_exp = p.c_exp;
-  const int krow_perm = swap_bits23(lq);
 
+  f32x16 scur[C::KBLK];   // raw scores of the tile being finished
   if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    if (n_tiles > 1) {
+      load_k(C::BC);
+      store_k(1);
+    }
   }
   // Drain every outstanding global load (the Q fragments included) before the loop,
-  // so inside it the only loads in flight are the next tile's prefetch and no
-  // matrix instruction waits on them.  Encoding: vmcnt(0), expcnt and lgkmcnt
-  // unconstrained.
+  // so inside it the only loads in flight are prefetches and no matrix instruction
+  // waits on them.  Encoding: vmcnt(0), expcnt and lgkmcnt unconstrained.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
+  if (n_tiles > 0) qk(0, scur);
+  __syncthreads();  // K buffer 0 is rewritten in iteration 0
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // One iteration of the key loop.  LAST (the final tile) has no next tile to
+  // score; keeping it a compile-time case leaves the steady-state body free of
+  // branches around the matrix work.
+  auto iteration = [&](const int t, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
     const int j0 = t * C::BC;
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(j0 + C::BC);
+    if (!LAST) {
+      if (t + 2 < n_tiles) load_k(j0 + 2 * C::BC);
+      load_v(j0 + C::BC);
+    }
 
-    if (j0 < wave_end) {
-      const unsigned short* ks = smem + buf * C::K_ELEMS;
-      const unsigned short* vt = smem + 2 * C::K_ELEMS + buf * C::V_ELEMS;
-      // S^T = K Q^T for the tile, fp32 accumulation.  The K fragments of the next
-      // 32-key block are read from LDS before the MFMAs of the current one are
-      // issued, so LDS latency hides behind matrix work.
-      f32x16 sacc[C::KBLK];
-      bf16x8 kf[2][C::DSTEPS];
-      const unsigned short* kbase = ks + krow_perm * C::KSTR + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < C::DSTEPS; ++s) kf[0][s] = *(const bf16x8*)(kbase + 16 * s);
-#pragma unroll
-      for (int kb = 0; kb < C::KBLK; ++kb) {
-        if (kb + 1 < C::KBLK) {
-#pragma unroll
-          for (int s = 0; s < C::DSTEPS; ++s)
-            kf[(kb + 1) & 1][s] = *(const bf16x8*)(kbase + (kb + 1) * 32 * C::KSTR + 16 * s);
-        }
-        sacc[kb] = (f32x16){};
-#pragma unroll
-        for (int s = 0; s < C::DSTEPS; ++s)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][s], qf[s], sacc[kb], 0, 0, 0);
-      }
-      if (p.pre_scale) {
-#pragma unroll
-        for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] *= p.c_pre;
-      }
-      // mask: only tiles that reach past kv_len or cross the causal diagonal
-      const bool need_mask = (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + kb * 32 + 16 * (r >> 3) + 8 * lg + (r & 7);
-            const bool ok = key < L && (!p.causal || key <= qrow);
-            if (!ok) sacc[kb][r] = kNegInf;
-          }
-      }
-      // row maximum: in-lane, then with the partner lane holding the other 16 keys
-      float mx = kNegInf;
+    if (p.pre_scale) {
 #pragma unroll
       for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = max_with_partner(mx) * c_exp;
-      // Online correction.  The exponent reference m_run moves to the new maximum
-      // only when the maximum rises by more than kRescaleSlack (log2 units); until
-      // then the exponentials are taken against the older reference and stay
-      // <= 2^kRescaleSlack.  Numerator and normaliser always share one reference, so
-      // a / l is unchanged; moving the reference multiplies both by
-      // alpha = exp2(m_old - m_new), exactly the correction of the recurrence.
-      const bool move = mx > m_run + kRescaleSlack;
-      const float m_new = move ? mx : m_run;
-      // guard: a row with no valid key so far keeps m_new = -inf; use 0 as the
-      // exponent reference so that no -inf - (-inf) appears
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-
-      float lsum = 0.f;
+        for (int r = 0; r < 16; ++r) scur[kb][r] *= p.c_pre;
+    }
+    // mask: only tiles that reach past kv_len or cross the wave's causal diagonal
+    if ((j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw)) {
 #pragma unroll
       for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c_exp, -m_use));
-          sacc[kb][r] = e;
-          lsum += e;
+          const int key = j0 + kb * 32 + 16 * (r >> 3) + 8 * lg + (r & 7);
+          const bool ok = key < L && (!p.causal || key <= qrow);
+          if (!ok) scur[kb][r] = kNegInf;
         }
-      if (__any(move)) {
-        // alpha == 1 exactly on rows whose reference did not move
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < C::DBLK; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-      }
-      l_run += lsum;
-
-      // P -> bf16, laid out as the B operand of O^T = V^T P^T
-      bf16x8 pf[C::KBLK][2];
-#pragma unroll
-      for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 w;
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            w[x] = pack_bf16x2(sacc[kb][8 * j + 2 * x], sacc[kb][8 * j + 2 * x + 1]);
-          pf[kb][j] = __builtin_bit_cast(bf16x8, w);
-        }
-      // O^T += V^T P^T, with the V^T fragments of the next 32 dimensions read ahead
-      bf16x8 vf[2][C::KBLK * 2];
-      const unsigned short* vbase = vt + lq * C::VSTR + 8 * lg;
-#pragma unroll
-      for (int x = 0; x < C::KBLK * 2; ++x) vf[0][x] = *(const bf16x8*)(vbase + 16 * x);
-#pragma unroll
-      for (int d = 0; d < C::DBLK; ++d) {
-        if (d + 1 < C::DBLK) {
-#pragma unroll
-          for (int x = 0; x < C::KBLK * 2; ++x)
-            vf[(d + 1) & 1][x] = *(const bf16x8*)(vbase + (d + 1) * 32 * C::VSTR + 16 * x);
-        }
-#pragma unroll
-        for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[d & 1][2 * kb + j], pf[kb][j],
-                                                              oacc[d], 0, 0, 0);
-      }
     }
 
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+    // row maximum: in-lane, then with the partner lane holding the other 16 keys
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
+    mx = max_with_partner(mx) * c_exp;
+    // Online correction.  The exponent reference m_run moves to the new maximum when
+    // the maximum rises by more than kRescaleSlack (log2 units; 0 = on every rise).
+    // Numerator and normaliser always share one reference, so a / l is unchanged;
+    // moving the reference multiplies both by alpha = exp2(m_old - m_new), exactly
+    // the correction of the recurrence.
+    const bool move = mx > m_run + kRescaleSlack;
+    const float m_new = move ? mx : m_run;
+    // guard: a row with no valid key so far keeps m_new = -inf; use 0 as the
+    // exponent reference so that no -inf - (-inf) appears
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+
+    if (__any(move)) {
+      // alpha == 1 exactly on rows whose reference did not move
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+    }
+
+    // scores of the next tile: independent matrix work that overlaps the
+    // exponentials below (same basic block, so the scheduler can interleave them)
+    f32x16 snext[C::KBLK];
+    if (!LAST) qk((t + 1) & 1, snext);
+
+    // P = exp2(s*c - m), rounded to bf16 as the B operand of O^T = V^T P^T, and the
+    // row-sum part of this lane
+    bf16x8 pf[C::KBLK][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float e0 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(scur[kb][8 * j + 2 * x], c_exp, -m_use));
+          const float e1 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(scur[kb][8 * j + 2 * x + 1], c_exp, -m_use));
+          lsum += e0 + e1;
+          w[x] = pack_bf16x2(e0, e1);
+        }
+        pf[kb][j] = __builtin_bit_cast(bf16x8, w);
+      }
+    l_run += lsum;
+
+    // O^T += V^T P^T from V buffer t&1; consecutive matrix instructions go to
+    // different accumulators and share their B operand
+    const unsigned short* vbase = smem + 2 * C::K_ELEMS + (t & 1) * C::V_ELEMS +
+                                  lq * C::VSTR + 8 * lg;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d) {
+          const bf16x8 a = *(const bf16x8*)(vbase + d * 32 * C::VSTR + 32 * kb + 16 * j);
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][j], oacc[d], 0, 0, 0);
+        }
+
+    if (!LAST) {
+      if (t + 2 < n_tiles) store_k(t & 1);
+      store_v((t + 1) & 1);
+      __syncthreads();
+#pragma unroll
+      for (int kb = 0; kb < C::KBLK; ++kb) scur[kb] = snext[kb];
+    }
+  };
+
+  for (int t = 0; t + 1 < n_tiles; ++t) iteration(t, std::false_type{});
+  if (n_tiles > 0) iteration(n_tiles - 1, std::true_type{});
 
   // ---- epilogue: O = a / l (0 for rows with no valid key), LSE = ln2 (m + log2 l) ----
   const float l_tot = sum_with_partner(l_run);
