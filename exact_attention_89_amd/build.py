@@ -66,11 +66,22 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link failed")
+    _check_loads(tmp)
     os.replace(tmp, OUT)
     if verbose:
         sys.stdout.write("\n".join(log))
     _check_resources("\n".join(log))
     return OUT
+
+
+def _check_loads(path: str) -> None:
+    """dlopen the freshly linked library (in a child process, so this process never
+    maps it): an unresolved symbol, e.g. a kernel stub the host pass did not emit,
+    fails the build here rather than at first use."""
+    code = f"import ctypes; ctypes.CDLL({path!r})"
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"built library does not load: {r.stderr.strip()[-400:]}")
 
 
 def _check_resources(log: str) -> None:

@@ -7,32 +7,51 @@
 // loop"; page "Kernel Fusion and the Memory Wall", section "FlashAttention: avoid
 // the full score matrix").
 //
-// Work split: one workgroup = 4 waves = BR = 128 query rows of one (batch, head);
-// each wave owns 32 rows for the whole key loop.  Keys are streamed in tiles of
-// BC = 64 through LDS, double buffered: the global loads of tile t+1 are issued
-// before tile t is computed and written to the other LDS buffer after it.
+// Work split.  One workgroup = 4 waves = 128 query rows of one (batch, head); each
+// wave owns 32 rows for the whole key loop.  Keys are streamed in tiles of 64.  A
+// workgroup uses 64 KiB of LDS (D = 128) and at most 256 registers per lane, so two
+// workgroups (two waves per SIMD) share a CU and hide each other's latencies.
 //
-// Register layout (the core of the design).  A wave computes the TRANSPOSED score
-// tile S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the A operand is K (rows = keys,
-// from LDS), the B operand is Q^T (columns = queries, held in VGPRs for the whole
-// loop).  In the 32x32 accumulator, lane l holds query column l%32 and 16 key rows,
-// so each query's scores live in two lanes (l and l^32): the row maximum is an
-// in-lane max plus one exchange with lane l^32, the row sum stays per lane until the
-// epilogue, and the per-query rescale of the output is a per-lane scalar.
+// Register layout.  A wave computes the TRANSPOSED scores S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16: A = K (rows = keys, from LDS), B = Q^T (columns =
+// queries, in VGPRs for the whole loop).  Lane l then holds query l%32 and 16 keys,
+// so a row maximum is an in-lane max plus one exchange with lane l^32, the row sum
+// stays per lane until the epilogue, and the per-query rescale is a per-lane scalar.
+// The output is accumulated transposed, O^T = V^T P^T, with P taken straight from
+// the score registers as the B operand.  For that, accumulator row i holds key
+// swap_bits23(i) (bits 2 and 3 exchanged), so register r of lane l holds key
+// 16*(r/8) + 8*(l/32) + r%8 of its 32-key block: the 8 keys a lane contributes to
+// one P.V step are consecutive, and so is the matching V^T operand (one dimension,
+// 8 consecutive keys), a single 16-byte read from a transposed V tile.
 //
-// The output is accumulated transposed as well, O^T = V^T P^T, so P is consumed
-// straight from the score accumulator registers as the B operand: register 8j+t of
-// lane l supplies contraction slot (l/32, t) of the j-th 16-key step.  For that the
-// contraction slot of the A operand (V^T, read from LDS) must name the same key,
-// and the score rows are therefore produced in a permuted key order: accumulator
-// row i is key swap_bits23(i) (bits 2 and 3 of the row index exchanged).  With that
-// permutation register r of lane l holds key 16*(r/8) + 8*(l/32) + r%8 of its
-// 32-key block, so the 8 keys each lane contributes to a P.V step are consecutive
-// and the matching V^T operand is one 16-byte LDS read.  V is transposed once, on
-// its way into LDS ([D][BC] layout), so no transpose happens in the inner loop.
+// Data movement.  K tiles go from global memory straight into LDS (buffer_load ...
+// lds, no staging registers), row-major; V tiles pass through registers and are
+// written transposed ([D][64 keys]).  Both are double buffered: the loads of tile
+// t+1 are issued before tile t is computed.  In both layouts the 16-byte chunks of a
+// row are XOR-swizzled with a function of the row, so the fragment reads are
+// bank-conflict free (the lanes the LDS serves together touch each bank once).  The
+// key loop is unrolled by two, so the buffer of every LDS access is known at compile
+// time and every fragment address is a per-lane register computed once plus an
+// immediate offset: no address arithmetic in the loop.
 //
-// LDS rows are padded by 16 bytes so the 16-byte fragment reads of 16 lanes cover
-// all 64 banks without conflict.
+// Key tile t:
+//   a) issue the loads of K(t+1) (LDS) and V(t+1) (registers)
+//   b) S(t) = K(t) Q^T on the matrix cores
+//   c) mask S(t) if the tile reaches past kv_len or crosses the causal diagonal
+//   d) row maxima -> exponent reference m(t); if a reference moved, O and l are
+//      multiplied by alpha(t) (rare, see below)
+//   e) P(t) = exp2(S(t)*c - m(t)), its row sums and its bf16 packing
+//   f) O^T += V(t)^T P(t)^T on the matrix cores
+//   g) write V(t+1) transposed; barrier
+// The two workgroups on a CU interleave these phases, so one wave's exponentials
+// run while the other's matrix instructions do.
+//
+// Online correction, lazily: the exponent reference of a row moves to the new row
+// maximum only when the maximum exceeds it by more than kRescaleSlack (log2 units);
+// until then exponentials are taken against the older reference and stay
+// <= 2^kRescaleSlack.  Numerator and normaliser always share one reference, so
+// a / l is the same; when the reference moves both are multiplied by
+// alpha = exp2(m_old - m_new), the correction of the recurrence.
 
 #include <type_traits>
 
@@ -44,21 +63,35 @@ namespace {
 
 template <int D>
 struct Cfg {
-  static constexpr int BR = 128;           // query rows per workgroup
-  static constexpr int BC = 64;            // keys per tile
-  static constexpr int NT = 256;           // threads per workgroup (4 waves)
-  static constexpr int KSTR = D + 8;       // K tile row stride (bf16 elements)
-  static constexpr int VSTR = BC + 8;      // V^T tile row stride (bf16 elements)
-  static constexpr int K_ELEMS = BC * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int K_UNITS = BC * D / 8;          // 16-byte units of a K tile
-  static constexpr int K_PER_T = K_UNITS / NT;
-  static constexpr int V_UNITS = (BC / 4) * (D / 8);  // units of 4 keys x 8 dims
-  static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
-  static constexpr int DSTEPS = D / 16;    // k-steps of the S^T product
-  static constexpr int DBLK = D / 32;      // 32-row blocks of O^T
-  static constexpr int KBLK = BC / 32;     // 32-key blocks of a tile
+  static constexpr int BR = 128;                 // query rows per workgroup
+  static constexpr int BC = 64;                  // keys per tile
+  static constexpr int NT = 256;                 // threads per workgroup (4 waves)
+  static constexpr int ROWB = D * 2;             // bytes per K row
+  static constexpr int TILE = BC * ROWB;         // bytes per K tile (and per V^T tile)
+  static constexpr int VTROWB = BC * 2;          // bytes per V^T row (64 keys)
+  static constexpr int DMA = TILE / 1024 / 4;    // 1 KiB K loads per wave per tile
+  static constexpr int V_UNITS = (BC / 4) * (D / 8);  // threads staging V (4 keys x 8 dims)
+  static constexpr int DSTEPS = D / 16;          // k-steps of S^T = K Q^T
+  static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
+  static constexpr int KBLK = BC / 32;           // 32-key blocks of a tile
+  static constexpr int LDS = 4 * TILE;           // K double buffer, V^T double buffer
+  static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
 };
+
+// How far (log2 units) the row maximum may rise above the exponent reference before
+// the accumulators are corrected.
+constexpr float kRescaleSlack = 8.0f;
+
+// K chunk swizzle: the 16 lanes served together read one chunk column of 16
+// consecutive rows; a 128-dimension row spans all 64 banks, a 64-dimension row half.
+// Adding 32 to the row leaves it unchanged (so both 32-key blocks share offsets).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+// V^T rows are 64 keys (128 bytes, 8 chunks): two consecutive rows span the banks.
+// Adding 32 to the row leaves it unchanged.
+__device__ __forceinline__ int vtswz(int d) { return (d >> 1) & 7; }
 
 // v_permlane32_swap exchanges the upper half-wave of one operand with the lower
 // half-wave of the other; with both operands = x, the two results of every lane are
@@ -75,22 +108,25 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-#ifndef ATTN89_RESCALE_SLACK
-#define ATTN89_RESCALE_SLACK 0.0f
-#endif
-// How far (log2 units) the row maximum may rise above the exponent reference
-// before the accumulators are corrected; 0 corrects on every rise.
-constexpr float kRescaleSlack = ATTN89_RESCALE_SLACK;
-
 __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-template <int D>
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+template <typename T>
+__device__ __forceinline__ T lds_load(const lds_u8* base, unsigned off) {
+  return *(const __attribute__((address_space(3))) T*)(base + off);
+}
+
+// PRE: scale <= 0, so scores are scaled before they are masked (a separate
+// instantiation keeps that branch out of the common kernel).
+template <int D, bool PRE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short smem[2 * (C::K_ELEMS + C::V_ELEMS)];
-  // buffer x: K tile at smem + x*K_ELEMS, V^T tile at smem + 2*K_ELEMS + x*V_ELEMS
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+  lds_u8* const lds = (lds_u8*)smem;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -104,9 +140,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
   // head lands on the same XCD and its K/V re-reads stay in that XCD's L2.
   const int BH = p.B * p.H;
   const int n_qb = (p.Nq + C::BR - 1) / C::BR;
-  const int t_id = blockIdx.x;
-  const int qb = n_qb - 1 - t_id / BH;
-  const int bh = t_id % BH;
+  const int qb = n_qb - 1 - (int)blockIdx.x / BH;
+  const int bh = (int)blockIdx.x % BH;
   const int b = bh / p.H;
 
   const unsigned short* qp = (const unsigned short*)p.q + (size_t)bh * p.Nq * D;
@@ -120,96 +155,112 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
   const int q_hi = min(q0 + C::BR, p.Nq);
   const int kv_end = p.causal ? min(L, q_hi) : L;    // keys any row of the block sees
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
-  const int qw = q0 + wave * 32;
-
-  // ---- Q fragments: B operand of S^T = K Q^T, resident for the whole loop ----
-  // Buffer loads: rows past Nq (or keys past kv_len below) read as zeros.
+  const int qw = q0 + wave * 32;                     // first row of this wave
   const int qrow = qw + lq;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop ----
+  // Buffer loads: rows past Nq (and below, keys past kv_len) read as zeros.
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)p.Nq * D * 2);
   bf16x8 qf[C::DSTEPS];
 #pragma unroll
   for (int s = 0; s < C::DSTEPS; ++s)
-    qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, ((unsigned)qrow * D + 16 * s + 8 * lg) * 2));
+    qf[s] = __builtin_bit_cast(bf16x8,
+                               buffer_load16(qrs, ((unsigned)qrow * D + 16 * s + 8 * lg) * 2));
 
-  // ---- tile staging: global -> registers -> LDS ----
-  // K runs one tile ahead of V: while tile t is exponentiated and multiplied into O,
-  // the scores of tile t+1 are already being produced.  Iteration t reads K(t+1)
-  // from K buffer (t+1)&1 and V(t) from V buffer t&1, and writes K(t+2) into K
-  // buffer t&1 and V(t+1) into V buffer (t+1)&1; one barrier per iteration.
-  u32x4 kreg[C::K_PER_T];
-  u32x4 vreg[C::V_PER_T][4];
-
+  // ---- K: global -> LDS without registers ----
+  // Load n of this wave writes tile bytes [m*1024, m*1024 + 1024), m = wave*DMA + n,
+  // lane i the 16 bytes at m*1024 + 16*i; the lane fetches the global chunk the
+  // swizzle puts there.  The tile start is the scalar offset of the load.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)L * D * 2);
+  unsigned koff[C::DMA];
+#pragma unroll
+  for (int n = 0; n < C::DMA; ++n) {
+    const int byte = (wave * C::DMA + n) * 1024 + 16 * lane;
+    const int row = byte / C::ROWB;
+    const int ch = ((byte % C::ROWB) / 16) ^ kswz<D>(row);
+    koff[n] = ((unsigned)row * D + 8 * ch) * 2;
+  }
+  auto load_k = [&](int t, int stage) {
+#pragma unroll
+    for (int n = 0; n < C::DMA; ++n)
+      buffer_load16_to_lds(krs, (lds_void*)(lds + stage * C::TILE + (wave * C::DMA + n) * 1024),
+                           koff[n], t * C::BC * D * 2);
+  };
+
+  // ---- V: global -> registers -> LDS, transposed ----
+  // Thread (kg, dg) holds keys 4kg..4kg+3 x dimensions 8dg..8dg+7 (four 16-byte
+  // loads) and writes them as 8 rows of V^T, 4 keys (8 bytes) each.
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (unsigned)L * D * 2);
-  auto load_k = [&](int j0) {
+  const bool v_owner = C::V_UNITS >= C::NT || tid < C::V_UNITS;
+  const int vkg = tid % (C::BC / 4), vdg = tid / (C::BC / 4);
+  const unsigned vgoff = ((unsigned)(4 * vkg) * D + 8 * vdg) * 2;
+  unsigned vwoff[4];  // V^T byte offset of row 8dg + 2x (row 8dg + 2x + 1: + VTROWB)
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int c = tid + C::NT * i;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      kreg[i] = buffer_load16(krs, ((unsigned)(j0 + row) * D + col) * 2);
-    }
-  };
-  auto load_v = [&](int j0) {
+  for (int x = 0; x < 4; ++x) {
+    const int d = 8 * vdg + 2 * x;
+    vwoff[x] = d * C::VTROWB + (((vkg >> 1) ^ vtswz(d)) * 16) + (vkg & 1) * 8;
+  }
+  u32x4 vreg[4];
+  auto load_v = [&](int t) {
+    if (v_owner) {
 #pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = tid + C::NT * i;
-      const int kg = u % (C::BC / 4);
-      const int dg = u / (C::BC / 4);
-      if (u < C::V_UNITS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vreg[i][r] = buffer_load16(vrs, ((unsigned)(j0 + 4 * kg + r) * D + 8 * dg) * 2);
-      }
-    }
-  };
-  auto store_k = [&](int buf) {
-    unsigned short* ks = smem + buf * C::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int c = tid + C::NT * i;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      *(u32x4*)(ks + row * C::KSTR + col) = kreg[i];
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = buffer_load16_so(vrs, vgoff + r * D * 2, t * C::BC * D * 2);
     }
   };
   auto store_v = [&](int buf) {
-    unsigned short* vt = smem + 2 * C::K_ELEMS + buf * C::V_ELEMS;
+    if (v_owner) {
 #pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = tid + C::NT * i;
-      if (u < C::V_UNITS) {
-        const int kg = u % (C::BC / 4);
-        const int dg = u / (C::BC / 4);
-        // 4 keys x 8 dims in registers -> 8 rows of V^T, 4 consecutive keys each
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          const int sh = (e & 1) * 16;
-          const unsigned int a0 = (vreg[i][0][w] >> sh) & 0xFFFFu;
-          const unsigned int a1 = (vreg[i][1][w] >> sh) & 0xFFFFu;
-          const unsigned int a2 = (vreg[i][2][w] >> sh) & 0xFFFFu;
-          const unsigned int a3 = (vreg[i][3][w] >> sh) & 0xFFFFu;
-          u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
-          *(u32x2*)(vt + (8 * dg + e) * C::VSTR + 4 * kg) = pk;
-        }
+      for (int e = 0; e < 8; ++e) {
+        // row 8dg + e of V^T: dimension e of keys 4kg .. 4kg + 3
+        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 pk = {__builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel),
+                          __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel)};
+        *(__attribute__((address_space(3))) u32x2*)(
+            lds + C::VT0 + buf * C::TILE + vwoff[e >> 1] + (e & 1) * C::VTROWB) = pk;
       }
     }
   };
 
-  const int krow_perm = swap_bits23(lq);
-  // S^T = K Q^T for the 64 keys held in K buffer kbuf, fp32 accumulation
-  auto qk = [&](int kbuf, f32x16* sacc) {
-    const unsigned short* kbase = smem + kbuf * C::K_ELEMS + krow_perm * C::KSTR + 8 * lg;
+  // ---- fragment read offsets (per lane, fixed for the whole loop) ----
+  const int krow = swap_bits23(lq);   // key (row of K) this lane feeds to the MFMA
+  unsigned kro[C::DSTEPS];
 #pragma unroll
-    for (int kb = 0; kb < C::KBLK; ++kb) sacc[kb] = (f32x16){};
-    // consecutive matrix instructions go to different accumulators
+  for (int s = 0; s < C::DSTEPS; ++s)
+    kro[s] = krow * C::ROWB + (((2 * s + lg) ^ kswz<D>(krow)) * 16);
+  unsigned vro[C::KBLK * 2];
+#pragma unroll
+  for (int x = 0; x < C::KBLK * 2; ++x)
+    vro[x] = lq * C::VTROWB + (((2 * x + lg) ^ vtswz(lq)) * 16);
+
+  // S^T = K Q^T for the tile in K buffer `stage`, fp32 accumulation from 0
+  auto qk = [&](int stage, f32x16* sacc) {
 #pragma unroll
     for (int s = 0; s < C::DSTEPS; ++s)
 #pragma unroll
       for (int kb = 0; kb < C::KBLK; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(kbase + kb * 32 * C::KSTR + 16 * s);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+        const bf16x8 a =
+            lds_load<bf16x8>(lds + stage * C::TILE + kb * 32 * C::ROWB, kro[s]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, qf[s], s == 0 ? (f32x16){} : sacc[kb], 0, 0, 0);
+      }
+  };
+
+  // mask of tile t: -inf for keys past kv_len and keys above the causal diagonal
+  auto needs_mask = [&](int t) {
+    const int j0 = t * C::BC;
+    return PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw);
+  };
+  auto apply_mask = [&](int t, f32x16* sacc) {
+    const int j0 = t * C::BC;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + kb * 32 + 16 * (r >> 3) + 8 * lg + (r & 7);
+        const bool ok = key < L && (!p.causal || key <= qrow);
+        const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
+        sacc[kb][r] = ok ? x : kNegInf;
       }
   };
 
@@ -217,94 +268,45 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
   f32x16 oacc[C::DBLK];
 #pragma unroll
   for (int d = 0; d < C::DBLK; ++d) oacc[d] = (f32x16){};
-  float m_run = kNegInf;  // exponent reference: running max of s*c (log2 domain)
+  float m_run = kNegInf;  // exponent reference (log2 domain)
   float l_run = 0.f;      // this lane's part of the running sum
   const float c_exp = p.c_exp;
 
-  f32x16 scur[C::KBLK];   // raw scores of the tile being finished
-  if (n_tiles > 0) {
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-    if (n_tiles > 1) {
-      load_k(C::BC);
-      store_k(1);
-    }
-  }
-  // Drain every outstanding global load (the Q fragments included) before the loop,
-  // so inside it the only loads in flight are prefetches and no matrix instruction
-  // waits on them.  Encoding: vmcnt(0), expcnt and lgkmcnt unconstrained.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  if (n_tiles > 0) qk(0, scur);
-  __syncthreads();  // K buffer 0 is rewritten in iteration 0
-
-  // One iteration of the key loop.  LAST (the final tile) has no next tile to
-  // score; keeping it a compile-time case leaves the steady-state body free of
-  // branches around the matrix work.
-  auto iteration = [&](const int t, auto last_tag) {
+  // ---- one key tile; PAR = t & 1 selects the buffers at compile time ----
+  auto iteration = [&](const int t, auto par_tag, auto last_tag) {
+    constexpr int PAR = decltype(par_tag)::value;
     constexpr bool LAST = decltype(last_tag)::value;
-    const int j0 = t * C::BC;
+    // a) prefetch the next tile
     if (!LAST) {
-      if (t + 2 < n_tiles) load_k(j0 + 2 * C::BC);
-      load_v(j0 + C::BC);
+      load_k(t + 1, PAR ^ 1);
+      load_v(t + 1);
     }
-
-    if (p.pre_scale) {
-#pragma unroll
-      for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) scur[kb][r] *= p.c_pre;
-    }
-    // mask: only tiles that reach past kv_len or cross the wave's causal diagonal
-    if ((j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw)) {
-#pragma unroll
-      for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + kb * 32 + 16 * (r >> 3) + 8 * lg + (r & 7);
-          const bool ok = key < L && (!p.causal || key <= qrow);
-          if (!ok) scur[kb][r] = kNegInf;
-        }
-    }
-
-    // row maximum: in-lane, then with the partner lane holding the other 16 keys
+    // b) scores; c) mask
+    f32x16 scur[C::KBLK];
+    qk(PAR, scur);
+    if (needs_mask(t)) apply_mask(t, scur);
+    // d) row maximum (in-lane, then with the partner lane) and the new reference;
+    //    guard: a row with no valid key so far keeps m = -inf and uses 0 as its
+    //    exponent reference, so no -inf - (-inf) is ever formed
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
     mx = max_with_partner(mx) * c_exp;
-    // Online correction.  The exponent reference m_run moves to the new maximum when
-    // the maximum rises by more than kRescaleSlack (log2 units; 0 = on every rise).
-    // Numerator and normaliser always share one reference, so a / l is unchanged;
-    // moving the reference multiplies both by alpha = exp2(m_old - m_new), exactly
-    // the correction of the recurrence.
     const bool move = mx > m_run + kRescaleSlack;
     const float m_new = move ? mx : m_run;
-    // guard: a row with no valid key so far keeps m_new = -inf; use 0 as the
-    // exponent reference so that no -inf - (-inf) appears
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-
     if (__any(move)) {
-      // alpha == 1 exactly on rows whose reference did not move
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < C::DBLK; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
     }
-
-    // scores of the next tile: independent matrix work that overlaps the
-    // exponentials below (same basic block, so the scheduler can interleave them)
-    f32x16 snext[C::KBLK];
-    if (!LAST) qk((t + 1) & 1, snext);
-
-    // P = exp2(s*c - m), rounded to bf16 as the B operand of O^T = V^T P^T, and the
-    // row-sum part of this lane
+    m_run = m_new;
+    // e) P = exp2(s*c - m), rounded to bf16 in the B-operand layout of O^T = V^T P^T
     bf16x8 pf[C::KBLK][2];
     float lsum = 0.f;
 #pragma unroll
@@ -314,8 +316,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
         u32x4 w;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const float e0 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(scur[kb][8 * j + 2 * x], c_exp, -m_use));
+          const float e0 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * j + 2 * x], c_exp, -m_use));
           const float e1 = __builtin_amdgcn_exp2f(
               __builtin_fmaf(scur[kb][8 * j + 2 * x + 1], c_exp, -m_use));
           lsum += e0 + e1;
@@ -324,32 +326,44 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
         pf[kb][j] = __builtin_bit_cast(bf16x8, w);
       }
     l_run += lsum;
-
-    // O^T += V^T P^T from V buffer t&1; consecutive matrix instructions go to
-    // different accumulators and share their B operand
-    const unsigned short* vbase = smem + 2 * C::K_ELEMS + (t & 1) * C::V_ELEMS +
-                                  lq * C::VSTR + 8 * lg;
+    // f) O^T += V^T P^T from V^T buffer PAR
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int d = 0; d < C::DBLK; ++d) {
-          const bf16x8 a = *(const bf16x8*)(vbase + d * 32 * C::VSTR + 32 * kb + 16 * j);
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][j], oacc[d], 0, 0, 0);
+          const bf16x8 va = lds_load<bf16x8>(
+              lds + C::VT0 + PAR * C::TILE + d * 32 * C::VTROWB, vro[2 * kb + j]);
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][j], oacc[d], 0, 0, 0);
         }
-
+    // g) V(t+1) into V^T buffer PAR^1; the next tile must be in LDS before any wave
+    //    goes on
     if (!LAST) {
-      if (t + 2 < n_tiles) store_k(t & 1);
-      store_v((t + 1) & 1);
+      store_v(PAR ^ 1);
       __syncthreads();
-#pragma unroll
-      for (int kb = 0; kb < C::KBLK; ++kb) scur[kb] = snext[kb];
     }
   };
 
-  for (int t = 0; t + 1 < n_tiles; ++t) iteration(t, std::false_type{});
-  if (n_tiles > 0) iteration(n_tiles - 1, std::true_type{});
+  // ---- prologue: K(0) and V(0) in LDS ----
+  if (n_tiles > 0) {
+    load_v(0);
+    load_k(0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
+  if (n_tiles > 0) store_v(0);
+  __syncthreads();
+  int t = 0;
+  for (; t + 2 < n_tiles; t += 2) {
+    iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
+    iteration(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  if (t + 1 < n_tiles) {
+    iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
+    iteration(t + 1, std::integral_constant<int, 1>{}, std::true_type{});
+  } else if (t < n_tiles) {
+    iteration(t, std::integral_constant<int, 0>{}, std::true_type{});
+  }
 
   // ---- epilogue: O = a / l (0 for rows with no valid key), LSE = ln2 (m + log2 l) ----
   const float l_tot = sum_with_partner(l_run);
@@ -376,10 +390,17 @@ int launch_attn_fwd_bf16(const FwdArgs& a, int D, hipStream_t stream) {
   const int n_qb = (a.Nq + 127) / 128;
   const long long grid = (long long)n_qb * a.B * a.H;
   if (grid > 0x7fffffffLL) return -8;
+  const dim3 g((unsigned)grid), blk(256);
   if (D == 128) {
-    attn_fwd_bf16_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
+    if (a.pre_scale)
+      attn_fwd_bf16_kernel<128, true><<<g, blk, 0, stream>>>(a);
+    else
+      attn_fwd_bf16_kernel<128, false><<<g, blk, 0, stream>>>(a);
   } else {
-    attn_fwd_bf16_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
+    if (a.pre_scale)
+      attn_fwd_bf16_kernel<64, true><<<g, blk, 0, stream>>>(a);
+    else
+      attn_fwd_bf16_kernel<64, false><<<g, blk, 0, stream>>>(a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }

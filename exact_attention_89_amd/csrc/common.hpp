@@ -60,6 +60,20 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigne
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 16 bytes at byte offset voff + soff (soff wave-uniform, in a scalar register)
+__device__ __forceinline__ u32x4 buffer_load16_so(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                                  int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Global -> LDS without registers: lane i's 16 bytes from byte offset voff + soff
+// land at LDS address lds + 16*i (lds wave-uniform).
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r,
+                                                     __attribute__((address_space(3))) void* lds,
+                                                     unsigned voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
   return __uint_as_float(((unsigned int)h) << 16);
 }

@@ -50,7 +50,7 @@ def cmd_run(a):
     api.load_library()
     dev = torch.device("cuda:0")
     torch.manual_seed(0)
-    manifest = {"impl": a.impl, "calls": a.calls, "entries": []}
+    manifest = {"impl": a.label or a.impl, "calls": a.calls, "entries": []}
     if a.impl == "copy":
         n = a.copy_mib * (1 << 20) // 4
         x = torch.ones(n, dtype=torch.float32, device=dev)
@@ -116,7 +116,7 @@ def _read_counters(path_glob):
 
 def cmd_summarize(a):
     res = {}
-    for impl in ("copy", "fused", "materialized"):
+    for impl in ("copy", "fused", "materialized", "headline"):
         mpath = os.path.join(a.dir, impl, "manifest.json")
         if not os.path.exists(mpath):
             continue
@@ -148,6 +148,19 @@ def cmd_summarize(a):
                "write_factor": c["bytes_written"] / c["write_bytes"]}
     res["calibration"] = cal
     res["commands"] = a.command or []
+    if a.headline_json and "headline" in res and cal:
+        e = res["headline"]["entries"][0]
+        rd = e["fetch_bytes"] * cal["fetch_factor"]
+        wr = e["write_bytes"] * cal["write_factor"]
+        rec = {"workload": a.headline_name,
+               "fused": {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                         "algorithmic_bytes": e["algorithmic_bytes"],
+                         "kernel_source_hash": res["headline"]["kernel_source_hash"]},
+               "calibration": cal, "commands": a.command or []}
+        with open(a.headline_json, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"headline: read {rd / 2**20:.1f} MiB, write {wr / 2**20:.1f} MiB per launch "
+              f"(algorithmic {e['algorithmic_bytes'] / 2**20:.1f} MiB)")
     with open(a.out_json, "w") as f:
         json.dump(res, f, indent=1)
     # Markdown table
@@ -191,6 +204,7 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--impl", choices=["fused", "materialized", "copy"], required=True)
+    r.add_argument("--label", default=None, help="manifest label (e.g. headline)")
     r.add_argument("--N", type=int, nargs="+", default=[1024, 2048, 4096, 8192, 16384, 32768])
     r.add_argument("--causal", type=int, nargs="+", default=[1, 0])
     r.add_argument("--B", type=int, default=1)
@@ -204,6 +218,8 @@ def main():
     s.add_argument("--out-json", required=True)
     s.add_argument("--out-md", required=True)
     s.add_argument("--command", action="append")
+    s.add_argument("--headline-json", default=None)
+    s.add_argument("--headline-name", default="bf16_causal_b1h32_n8192_d128")
     a = ap.parse_args()
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
