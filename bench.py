@@ -18,7 +18,6 @@ Prints ONE JSON line:
 """
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -30,7 +29,6 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
-KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_89_amd", "csrc", "attn_fwd_bf16.hip")
 
 
 def log(msg):
@@ -39,11 +37,9 @@ def log(msg):
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    for fn in ("attn_fwd_bf16.hip", "common.hpp"):
-        with open(os.path.join(ROOT, "exact_attention_89_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the bf16 kernel sources: a traffic record taken from other sources is stale."""
+    from exact_attention_89_amd.traffic import _kernel_hash
+    return _kernel_hash()
 
 
 def measured_traffic(workload):
@@ -92,7 +88,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -24,6 +24,11 @@ _STATUS_NAMES = {
     -7: "ATTN_ERR_HIP", -8: "ATTN_ERR_TOO_LARGE",
 }
 
+# bf16 forward kernel choice (attn_fwd_select_kernel)
+ATTN_KERNEL_AUTO = 0
+ATTN_KERNEL_PINGPONG = 1
+ATTN_KERNEL_FOURWAVE = 2
+
 # exported symbol -> (restype, argtypes); must match include/attn.h
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -31,6 +36,7 @@ _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 EXPORTS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "attn_fwd_select_kernel": (_I, [_I]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
     "attn_materialized_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "attn_materialized": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ,
@@ -129,6 +135,14 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_le
     """Fused attention forward, bf16 in/out, fp32 LSE.  Returns (o, lse)."""
     import torch
     return _call_fwd("attn_fwd", q, k, v, scale, causal, kv_lens, out, lse, torch.bfloat16)
+
+
+def attn_fwd_select_kernel(which: int) -> int:
+    """Choose the bf16 forward kernel (ATTN_KERNEL_*); returns the previous choice."""
+    st = load_library().attn_fwd_select_kernel(int(which))
+    if st < 0:
+        raise AttnError(st, "attn_fwd_select_kernel")
+    return st
 
 
 def attn_fwd_f32(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_lens=None,

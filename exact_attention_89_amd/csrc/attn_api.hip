@@ -62,6 +62,32 @@ attn89::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, 
   return a;
 }
 
+// Which bf16 forward kernel attn_fwd launches (attn_fwd_select_kernel).
+int g_bf16_kernel = ATTN_KERNEL_AUTO;
+
+// Compute units of the current device, cached per device.
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+// The 8-wave ping-pong kernel (one 256-row workgroup per CU) is the faster one once
+// its grid covers every CU; below that, and for D = 64 (where the softmax, not the
+// matrix work, bounds a tile), the 4-wave kernel with twice as many workgroups wins.
+int pick_bf16_kernel(int B, int H, int Nq, int D) {
+  if (g_bf16_kernel != ATTN_KERNEL_AUTO) return g_bf16_kernel;
+  const long long pp_grid = (long long)((Nq + 255) / 256) * B * H;
+  return (D == 128 && pp_grid >= num_cus()) ? ATTN_KERNEL_PINGPONG : ATTN_KERNEL_FOURWAVE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,7 +103,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
       ((size_t)Nk + 256) * D * 2 >= ((size_t)1 << 31))
     return ATTN_ERR_TOO_LARGE;
   attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
-  return attn89::launch_attn_fwd_bf16(a, D, (hipStream_t)stream);
+  if (pick_bf16_kernel(B, H, Nq, D) == ATTN_KERNEL_PINGPONG)
+    return attn89::launch_attn_fwd_bf16_pp(a, D, (hipStream_t)stream);
+  return attn89::launch_attn_fwd_bf16_4w(a, D, (hipStream_t)stream);
+}
+
+int attn_fwd_select_kernel(int which) {
+  if (which != ATTN_KERNEL_AUTO && which != ATTN_KERNEL_PINGPONG &&
+      which != ATTN_KERNEL_FOURWAVE)
+    return ATTN_ERR_UNSUPPORTED;
+  const int prev = g_bf16_kernel;
+  g_bf16_kernel = which;
+  return prev;
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
@@ -124,6 +161,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 }  // extern "C"

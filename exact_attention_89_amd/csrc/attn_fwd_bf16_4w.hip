@@ -1,4 +1,6 @@
-// attn_fwd_bf16.hip -- the fused attention forward for gfx950, bf16 in / bf16 out.
+// attn_fwd_bf16_4w.hip -- the fused attention forward for gfx950, bf16 in / bf16 out,
+// 4-wave workgroups, two per CU (head dimension 64, and grids too small for the
+// 8-wave ping-pong kernel of attn_fwd_bf16_pp.hip to fill the GPU).
 //
 // One kernel computes O = softmax(Q K^T * scale + mask) V and the LSE.  The score
 // tile, its row maximum and sum, the exponentials, the online correction
@@ -12,17 +14,9 @@
 // workgroup uses 64 KiB of LDS (D = 128) and at most 256 registers per lane, so two
 // workgroups (two waves per SIMD) share a CU and hide each other's latencies.
 //
-// Register layout.  A wave computes the TRANSPOSED scores S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16: A = K (rows = keys, from LDS), B = Q^T (columns =
-// queries, in VGPRs for the whole loop).  Lane l then holds query l%32 and 16 keys,
-// so a row maximum is an in-lane max plus one exchange with lane l^32, the row sum
-// stays per lane until the epilogue, and the per-query rescale is a per-lane scalar.
-// The output is accumulated transposed, O^T = V^T P^T, with P taken straight from
-// the score registers as the B operand.  For that, accumulator row i holds key
-// swap_bits23(i) (bits 2 and 3 exchanged), so register r of lane l holds key
-// 16*(r/8) + 8*(l/32) + r%8 of its 32-key block: the 8 keys a lane contributes to
-// one P.V step are consecutive, and so is the matching V^T operand (one dimension,
-// 8 consecutive keys), a single 16-byte read from a transposed V tile.
+// Register and LDS layouts (transposed scores, P straight from the score registers,
+// swizzled K and V^T tiles) and the lazy online correction are described in
+// attn_bf16_tiles.hpp.
 //
 // Data movement.  K tiles go from global memory straight into LDS (buffer_load ...
 // lds, no staging registers), row-major; V tiles pass through registers and are
@@ -39,23 +33,16 @@
 //   b) S(t) = K(t) Q^T on the matrix cores
 //   c) mask S(t) if the tile reaches past kv_len or crosses the causal diagonal
 //   d) row maxima -> exponent reference m(t); if a reference moved, O and l are
-//      multiplied by alpha(t) (rare, see below)
+//      multiplied by alpha(t) (rare, see attn_bf16_tiles.hpp)
 //   e) P(t) = exp2(S(t)*c - m(t)), its row sums and its bf16 packing
 //   f) O^T += V(t)^T P(t)^T on the matrix cores
 //   g) write V(t+1) transposed; barrier
 // The two workgroups on a CU interleave these phases, so one wave's exponentials
 // run while the other's matrix instructions do.
 //
-// Online correction, lazily: the exponent reference of a row moves to the new row
-// maximum only when the maximum exceeds it by more than kRescaleSlack (log2 units);
-// until then exponentials are taken against the older reference and stay
-// <= 2^kRescaleSlack.  Numerator and normaliser always share one reference, so
-// a / l is the same; when the reference moves both are multiplied by
-// alpha = exp2(m_old - m_new), the correction of the recurrence.
-
 #include <type_traits>
 
-#include "common.hpp"
+#include "attn_bf16_tiles.hpp"
 #include "launch.hpp"
 
 namespace attn89 {
@@ -78,52 +65,10 @@ struct Cfg {
   static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
 };
 
-// How far (log2 units) the row maximum may rise above the exponent reference before
-// the accumulators are corrected.
-constexpr float kRescaleSlack = 8.0f;
-
-// K chunk swizzle: the 16 lanes served together read one chunk column of 16
-// consecutive rows; a 128-dimension row spans all 64 banks, a 64-dimension row half.
-// Adding 32 to the row leaves it unchanged (so both 32-key blocks share offsets).
-template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-// V^T rows are 64 keys (128 bytes, 8 chunks): two consecutive rows span the banks.
-// Adding 32 to the row leaves it unchanged.
-__device__ __forceinline__ int vtswz(int d) { return (d >> 1) & 7; }
-
-// v_permlane32_swap exchanges the upper half-wave of one operand with the lower
-// half-wave of the other; with both operands = x, the two results of every lane are
-// x[l] and x[l ^ 32] (in some order), so their max / sum is the two-lane reduction.
-__device__ __forceinline__ float max_with_partner(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float sum_with_partner(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ int swap_bits23(int i) {
-  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-
-template <typename T>
-__device__ __forceinline__ T lds_load(const lds_u8* base, unsigned off) {
-  return *(const __attribute__((address_space(3))) T*)(base + off);
-}
-
 // PRE: scale <= 0, so scores are scaled before they are masked (a separate
 // instantiation keeps that branch out of the common kernel).
 template <int D, bool PRE>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
   lds_u8* const lds = (lds_u8*)smem;
@@ -258,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + kb * 32 + 16 * (r >> 3) + 8 * lg + (r & 7);
-        const bool ok = key < L && (!p.causal || key <= qrow);
+        const bool ok = (key < L) & (!p.causal | (key <= qrow));
         const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
         sacc[kb][r] = ok ? x : kNegInf;
       }
@@ -386,21 +331,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs p) {
 
 }  // namespace
 
-int launch_attn_fwd_bf16(const FwdArgs& a, int D, hipStream_t stream) {
+int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream) {
   const int n_qb = (a.Nq + 127) / 128;
   const long long grid = (long long)n_qb * a.B * a.H;
   if (grid > 0x7fffffffLL) return -8;
   const dim3 g((unsigned)grid), blk(256);
   if (D == 128) {
     if (a.pre_scale)
-      attn_fwd_bf16_kernel<128, true><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<128, true><<<g, blk, 0, stream>>>(a);
     else
-      attn_fwd_bf16_kernel<128, false><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<128, false><<<g, blk, 0, stream>>>(a);
   } else {
     if (a.pre_scale)
-      attn_fwd_bf16_kernel<64, true><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<64, true><<<g, blk, 0, stream>>>(a);
     else
-      attn_fwd_bf16_kernel<64, false><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<64, false><<<g, blk, 0, stream>>>(a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }

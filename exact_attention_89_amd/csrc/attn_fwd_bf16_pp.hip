@@ -1,0 +1,415 @@
+// attn_fwd_bf16_pp.hip -- the fused attention forward for gfx950, bf16 in / bf16 out,
+// 8-wave "ping-pong" workgroups (head dimension 128, grids that fill the GPU).
+//
+// One kernel computes O = softmax(Q K^T * scale + mask) V and the LSE.  The score
+// tile, its row maximum and sum, the exponentials, the online correction
+// exp(m_old - m_new) and the P.V product never leave the workgroup (page
+// "Attention softmax fusion", sections "What fused has to mean" and "The tile
+// loop"; page "Kernel Fusion and the Memory Wall", section "FlashAttention: avoid
+// the full score matrix").
+//
+// Work split.  One workgroup = 8 waves = 256 query rows of one (batch, head); each
+// wave owns 32 rows for the whole key loop, and all 8 waves share each 64-key K/V
+// tile in LDS.  Waves w and w+4 run on the same SIMD.  They form two groups,
+// G0 = waves 0-3 and G1 = waves 4-7, that run the same loop half a tile apart
+// ("ping-pong"): while one group issues its matrix instructions (P.V of the
+// previous tile and Q.K^T of this one), the other computes its softmax on the
+// vector ALU.  A workgroup barrier between phases keeps the two groups in step, so
+// the matrix cores of every SIMD see one group's MFMA stream at all times and the
+// vector work of the other group hides behind it.
+//
+//   phase   G0                          G1
+//   0       S(0) = K(0) Q^T             (loads K(1))
+//   1       softmax(0) -> P(0)          S(0)
+//   2       O += V(0) P(0); S(1)        softmax(0)
+//   3       softmax(1)                  O += V(0) P(0); S(1)
+//   ...     (every phase ends with a workgroup barrier)
+//
+// Register and LDS layouts (transposed scores, P straight from the score registers,
+// swizzled K and V^T tiles) and the lazy online correction are described in
+// attn_bf16_tiles.hpp.
+//
+// Data movement.  G1 moves K tiles from global memory straight into LDS
+// (buffer_load ... lds, no staging registers), row-major; G0 loads V tiles into
+// registers and writes them transposed ([D][64 keys]) during its softmax phase.
+// Both are double buffered and requested two phases before first use.  In both
+// layouts the 16-byte chunks of a row are XOR-swizzled with a function of the row,
+// so the fragment reads are bank-conflict free.  Buffer indices are compile-time
+// constants (the loop is unrolled by two), so every fragment address is a per-lane
+// register computed once plus an immediate offset.
+
+#include <type_traits>
+
+#include "attn_bf16_tiles.hpp"
+#include "launch.hpp"
+
+namespace attn89 {
+namespace {
+
+template <int D>
+struct Cfg {
+  static constexpr int BR = 256;                 // query rows per workgroup
+  static constexpr int BC = 64;                  // keys per tile
+  static constexpr int NT = 512;                 // threads per workgroup (8 waves)
+  static constexpr int ROWB = D * 2;             // bytes per K row
+  static constexpr int TILE = BC * ROWB;         // bytes per K tile (and per V^T tile)
+  static constexpr int VTROWB = BC * 2;          // bytes per V^T row (64 keys)
+  static constexpr int KDMA = TILE / 1024 / 4;   // 1 KiB K loads per G1 wave per tile
+  static constexpr int V_UNITS = (BC / 4) * (D / 8);  // G0 threads staging V (4 keys x 8 dims)
+  static constexpr int DSTEPS = D / 16;          // k-steps of S^T = K Q^T
+  static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
+  static constexpr int KBLK = BC / 32;           // 32-key blocks of a tile
+  static constexpr int LDS = 4 * TILE;           // K double buffer, V^T double buffer
+  static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
+  static_assert(V_UNITS <= 256, "V staging must fit in group 0");
+};
+
+// Phase boundary: this wave's LDS accesses are complete, then all 8 waves meet.
+// Outstanding global loads into registers stay in flight (a plain __syncthreads
+// would also wait for them).
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Instruction order of an MFMA phase with NR fragment reads and NR MFMAs: kPrefetch
+// reads first, then one read after every MFMA, so each fragment is requested
+// kPrefetch MFMAs (kPrefetch x 32 cycles) before it is needed.  Left to itself the
+// compiler issues each read just before its MFMA and the matrix core waits out the
+// LDS latency every time.
+constexpr int kPrefetch = 4;
+template <int NR>
+__device__ __forceinline__ void schedule_mfma_phase() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);   // LDS reads
+#pragma unroll
+  for (int i = 0; i < NR - kPrefetch; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
+}
+
+// The wave in its MFMA phase gets issue priority over its SIMD partner (which is in
+// its softmax phase), so the matrix core is refilled as soon as it frees up.
+__device__ __forceinline__ void mfma_priority() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void valu_priority() { __builtin_amdgcn_s_setprio(0); }
+
+// PRE: scale <= 0, so scores are scaled before they are masked (a separate
+// instantiation keeps that branch out of the common kernel).
+template <int D, bool PRE>
+__global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+  lds_u8* const lds = (lds_u8*)smem;
+
+  const int tid = threadIdx.x;
+  // wave-uniform values live in scalar registers, so branches on them are real
+  // branches (a barrier must never sit in a lane-masked region)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;     // 0: G0 (stages V), 1: G1 (moves K)
+  const int wg = wave & 3;       // wave inside its group
+  const int lane = tid & 63;
+  const int lq = lane & 31;      // query column inside the wave's 32 rows
+  const int lg = lane >> 5;      // half of the wave
+
+  // Schedule: consecutive workgroups take different (b, h) of the same query block,
+  // heaviest (last, for causal) query blocks first.  Workgroups are dispatched to
+  // the 8 XCDs round robin, so when B*H is a multiple of 8 every query block of a
+  // head lands on the same XCD and its K/V re-reads stay in that XCD's L2.
+  const int BH = p.B * p.H;
+  const int n_qb = (p.Nq + C::BR - 1) / C::BR;
+  const int qb = n_qb - 1 - (int)blockIdx.x / BH;
+  const int bh = (int)blockIdx.x % BH;
+  const int b = bh / p.H;
+
+  const unsigned short* qp = (const unsigned short*)p.q + (size_t)bh * p.Nq * D;
+  const unsigned short* kp = (const unsigned short*)p.k + (size_t)bh * p.Nk * D;
+  const unsigned short* vp = (const unsigned short*)p.v + (size_t)bh * p.Nk * D;
+  unsigned short* op = (unsigned short*)p.o + (size_t)bh * p.Nq * D;
+  float* lsep = p.lse + (size_t)bh * p.Nq;
+
+  const int L = clamp_len(p.kv_lens, b, p.Nk);      // valid keys of this sequence
+  const int q0 = qb * C::BR;
+  const int q_hi = min(q0 + C::BR, p.Nq);
+  const int kv_end = p.causal ? min(L, q_hi) : L;    // keys any row of the block sees
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  const int qw = q0 + wave * 32;                     // first row of this wave
+  const int qrow = qw + lq;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop ----
+  // Buffer loads: rows past Nq (and below, keys past kv_len) read as zeros.
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)p.Nq * D * 2);
+  bf16x8 qf[C::DSTEPS];
+#pragma unroll
+  for (int s = 0; s < C::DSTEPS; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8,
+                               buffer_load16(qrs, ((unsigned)qrow * D + 16 * s + 8 * lg) * 2));
+
+  // ---- K (G1): global -> LDS without registers ----
+  // Load n of G1 wave wg writes tile bytes [m*1024, m*1024 + 1024), m = wg*KDMA + n,
+  // lane i the 16 bytes at m*1024 + 16*i; the lane fetches the global chunk the
+  // swizzle puts there.  The tile start is the scalar offset of the load.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)L * D * 2);
+  unsigned koff[C::KDMA];
+#pragma unroll
+  for (int n = 0; n < C::KDMA; ++n) {
+    const int byte = (wg * C::KDMA + n) * 1024 + 16 * lane;
+    const int row = byte / C::ROWB;
+    const int ch = ((byte % C::ROWB) / 16) ^ kswz<D>(row);
+    koff[n] = ((unsigned)row * D + 8 * ch) * 2;
+  }
+  auto load_k = [&](int t, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < C::KDMA; ++n)
+      buffer_load16_to_lds(krs, (lds_void*)(lds + stage * C::TILE + (wg * C::KDMA + n) * 1024),
+                           koff[n], t * C::BC * D * 2);
+  };
+
+  // ---- V (G0): global -> registers -> LDS, transposed ----
+  // Thread (kg, dg) holds keys 4kg..4kg+3 x dimensions 8dg..8dg+7 (four 16-byte
+  // loads) and writes them as 8 rows of V^T, 4 keys (8 bytes) each.
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (unsigned)L * D * 2);
+  const bool v_owner = C::V_UNITS >= 256 || tid < C::V_UNITS;   // used by G0 only
+  const int vkg = tid % (C::BC / 4), vdg = (tid / (C::BC / 4)) % (D / 8);
+  const unsigned vgoff = ((unsigned)(4 * vkg) * D + 8 * vdg) * 2;
+  unsigned vwoff[4];  // V^T byte offset of row 8dg + 2x (row 8dg + 2x + 1: + VTROWB)
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int d = 8 * vdg + 2 * x;
+    vwoff[x] = d * C::VTROWB + (((vkg >> 1) ^ vtswz(d)) * 16) + (vkg & 1) * 8;
+  }
+  u32x4 vreg[4];
+  auto load_v = [&](int t) __attribute__((always_inline)) {
+    if (v_owner) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = buffer_load16_so(vrs, vgoff + r * D * 2, t * C::BC * D * 2);
+    }
+  };
+  auto store_v = [&](int buf) __attribute__((always_inline)) {
+    if (v_owner) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // row 8dg + e of V^T: dimension e of keys 4kg .. 4kg + 3
+        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 pk = {__builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel),
+                          __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel)};
+        *(__attribute__((address_space(3))) u32x2*)(
+            lds + C::VT0 + buf * C::TILE + vwoff[e >> 1] + (e & 1) * C::VTROWB) = pk;
+      }
+    }
+  };
+
+  // ---- fragment read offsets (per lane, fixed for the whole loop) ----
+  const int krow = swap_bits23(lq);   // key (row of K) this lane feeds to the MFMA
+  unsigned kro[C::DSTEPS];
+#pragma unroll
+  for (int s = 0; s < C::DSTEPS; ++s)
+    kro[s] = krow * C::ROWB + (((2 * s + lg) ^ kswz<D>(krow)) * 16);
+  unsigned vro[C::KBLK * 2];
+#pragma unroll
+  for (int x = 0; x < C::KBLK * 2; ++x)
+    vro[x] = lq * C::VTROWB + (((2 * x + lg) ^ vtswz(lq)) * 16);
+
+  // ---- running state: one query per lane (shared by lanes l and l^32) ----
+  f32x16 oacc[C::DBLK];
+#pragma unroll
+  for (int d = 0; d < C::DBLK; ++d) oacc[d] = (f32x16){};
+  f32x16 sacc[C::KBLK];   // S(t), from its MFMA phase to its softmax phase
+  bf16x8 pf[C::KBLK][2];  // P(t), from its softmax phase to the next MFMA phase
+  float m_run = kNegInf;  // exponent reference (log2 domain)
+  float l_run = 0.f;      // this lane's part of the running sum
+  const float c_exp = p.c_exp;
+
+  // S^T = K Q^T for the tile in K buffer `stage`, fp32 accumulation from 0
+  auto qk = [&](int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < C::DSTEPS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < C::KBLK; ++kb) {
+        const bf16x8 a =
+            lds_load<bf16x8>(lds + stage * C::TILE + kb * 32 * C::ROWB, kro[s]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, qf[s], s == 0 ? (f32x16){} : sacc[kb], 0, 0, 0);
+      }
+  };
+  // O^T += V^T P^T from V^T buffer `buf`
+  auto pv = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d) {
+          const bf16x8 va = lds_load<bf16x8>(
+              lds + C::VT0 + buf * C::TILE + d * 32 * C::VTROWB, vro[2 * kb + j]);
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][j], oacc[d], 0, 0, 0);
+        }
+  };
+
+  // softmax of tile t: mask, row maxima -> exponent reference, lazy correction of
+  // O and l, P = exp2(s*c - m) rounded to bf16 in the B-operand layout of P.V.
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * C::BC;
+    if (PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw)) {
+#pragma unroll
+      for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + kb * 32 + 16 * (r >> 3) + 8 * lg + (r & 7);
+          const bool ok = (key < L) & (!p.causal | (key <= qrow));
+          const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
+          sacc[kb][r] = ok ? x : kNegInf;
+        }
+    }
+    // guard: a row with no valid key so far keeps m = -inf and uses 0 as its
+    // exponent reference, so no -inf - (-inf) is ever formed
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = max_with_partner(mx) * c_exp;
+    const bool move = mx > m_run + kRescaleSlack;
+    const float m_new = move ? mx : m_run;
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    if (__any(move)) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+    }
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float e0 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * j + 2 * x], c_exp, -m_use));
+          const float e1 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sacc[kb][8 * j + 2 * x + 1], c_exp, -m_use));
+          lsum += e0 + e1;
+          w[x] = pack_bf16x2(e0, e1);
+        }
+        pf[kb][j] = __builtin_bit_cast(bf16x8, w);
+      }
+    l_run += lsum;
+  };
+
+  auto epilogue = [&]() __attribute__((always_inline)) {
+  // ---- epilogue: O = a / l (0 for rows with no valid key), LSE = ln2 (m + log2 l) ----
+  const float l_tot = sum_with_partner(l_run);
+  if (qrow < p.Nq) {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    unsigned short* orow = op + (size_t)qrow * D;
+#pragma unroll
+    for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 w = {pack_bf16x2(oacc[d][4 * a + 0] * inv, oacc[d][4 * a + 1] * inv),
+                   pack_bf16x2(oacc[d][4 * a + 2] * inv, oacc[d][4 * a + 3] * inv)};
+        *(u32x2*)(orow + d * 32 + 8 * a + 4 * lg) = w;
+      }
+    if (lg == 0) {
+      lsep[qrow] = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+  };
+
+  // One tile period of group G; PAR = t & 1 selects the buffers at compile time.
+  //   MFMA phase:    O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
+  //   softmax phase: P(t); G0 writes V(t) to V^T buffer PAR and requests V(t+1),
+  //                  G1 requests K(t+2) into K buffer PAR
+  auto period = [&](const int t, auto grp_tag, auto par_tag, auto first_tag)
+                    __attribute__((always_inline)) {
+    constexpr int G = decltype(grp_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
+    mfma_priority();
+    if (!FIRST) pv(PAR ^ 1);
+    qk(PAR);
+    schedule_mfma_phase<FIRST ? C::DSTEPS * C::KBLK : 2 * C::DSTEPS * C::KBLK>();
+    if (G == 1) wait_vm0();   // K(t+1) has landed: it is read after the barrier
+    phase_barrier();
+    valu_priority();
+    softmax(t);
+    if (G == 0) {
+      store_v(PAR);
+      if (t + 1 < n_tiles) load_v(t + 1);
+    } else {
+      if (t + 2 < n_tiles) load_k(t + 2, PAR);
+    }
+    phase_barrier();
+  };
+
+  // The whole key loop of one group, as straight-line code of its own: the two
+  // groups move different data, and one shared body would make the compiler merge
+  // their register states (and wait for loads the other group issued).
+  auto run_group = [&](auto grp_tag) __attribute__((always_inline)) {
+    constexpr int G = decltype(grp_tag)::value;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // prologue: K(0) in LDS, V(0) on its way
+    if (n_tiles > 0) {
+      if (G == 1) load_k(0, 0);
+      else load_v(0);
+    }
+    if (G == 1) wait_vm0();
+    phase_barrier();
+    if (n_tiles > 0) {
+      if (G == 1) {
+        // G1 starts one phase late; meanwhile it requests K(1)
+        if (n_tiles > 1) load_k(1, 1);
+        phase_barrier();
+      }
+      period(0, grp_tag, I0{}, std::true_type{});
+      int t = 1;
+      for (; t + 1 < n_tiles; t += 2) {
+        period(t, grp_tag, I1{}, std::false_type{});
+        period(t + 1, grp_tag, I0{}, std::false_type{});
+      }
+      if (t < n_tiles) period(t, grp_tag, I1{}, std::false_type{});
+      // last MFMA phase: O += V(n-1) P(n-1)
+      mfma_priority();
+      if ((n_tiles - 1) & 1) pv(1);
+      else pv(0);
+      valu_priority();
+      // G0 ends one phase early; it meets G1's last softmax barrier
+      if (G == 0) phase_barrier();
+    }
+    epilogue();
+  };
+
+  if (grp == 0) run_group(std::integral_constant<int, 0>{});
+  else run_group(std::integral_constant<int, 1>{});
+}
+
+}  // namespace
+
+int launch_attn_fwd_bf16_pp(const FwdArgs& a, int D, hipStream_t stream) {
+  const int n_qb = (a.Nq + 255) / 256;
+  const long long grid = (long long)n_qb * a.B * a.H;
+  if (grid > 0x7fffffffLL) return -8;
+  const dim3 g((unsigned)grid), blk(512);
+  if (D == 128) {
+    if (a.pre_scale)
+      attn_fwd_bf16_pp_kernel<128, true><<<g, blk, 0, stream>>>(a);
+    else
+      attn_fwd_bf16_pp_kernel<128, false><<<g, blk, 0, stream>>>(a);
+  } else {
+    if (a.pre_scale)
+      attn_fwd_bf16_pp_kernel<64, true><<<g, blk, 0, stream>>>(a);
+    else
+      attn_fwd_bf16_pp_kernel<64, false><<<g, blk, 0, stream>>>(a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+}  // namespace attn89

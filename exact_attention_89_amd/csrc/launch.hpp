@@ -9,7 +9,10 @@
 
 namespace attn89 {
 
-int launch_attn_fwd_bf16(const FwdArgs& a, int D, hipStream_t stream);
+// bf16 forward kernels: 8-wave ping-pong workgroups of 256 query rows (D = 128 only)
+// and 4-wave workgroups of 128 rows (any supported D).
+int launch_attn_fwd_bf16_pp(const FwdArgs& a, int D, hipStream_t stream);
+int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream);
 int launch_attn_fwd_f32(const FwdArgs& a, int D, hipStream_t stream);
 
 // Workspace layout of the materialised baseline: S (fp32) then P (bf16), both

@@ -37,7 +37,8 @@ ROOT = os.path.dirname(HERE)
 
 def _kernel_hash():
     h = hashlib.sha256()
-    for fn in ("attn_fwd_bf16.hip", "common.hpp"):
+    for fn in ("attn_fwd_bf16_pp.hip", "attn_fwd_bf16_4w.hip", "attn_bf16_tiles.hpp",
+               "common.hpp"):
         with open(os.path.join(HERE, "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -75,6 +75,28 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const int32_t* kv_lens, void* stream);
 
 /*
+ * attn_fwd_select_kernel -- which of the two bf16 forward kernels attn_fwd
+ * launches.  Both compute the same function with the same arithmetic (bitwise
+ * identical results); they differ only in how work is spread over the GPU:
+ *
+ *   ATTN_KERNEL_PINGPONG  8-wave workgroups of 256 query rows, two wave groups
+ *                         half a key tile apart (one on the matrix cores while
+ *                         the other computes its softmax); one workgroup per CU
+ *   ATTN_KERNEL_FOURWAVE  4-wave workgroups of 128 query rows, two per CU
+ *   ATTN_KERNEL_AUTO      (default) ping-pong when D = 128 and its grid,
+ *                         ceil(Nq/256)*B*H workgroups, covers every compute
+ *                         unit; otherwise four-wave
+ *
+ * The setting is process-wide and not synchronised: change it only while no
+ * other thread calls attn_fwd.  Returns the previous setting, or
+ * ATTN_ERR_UNSUPPORTED (setting unchanged) for any other value of `which`.
+ */
+#define ATTN_KERNEL_AUTO      0
+#define ATTN_KERNEL_PINGPONG  1
+#define ATTN_KERNEL_FOURWAVE  2
+int attn_fwd_select_kernel(int which);
+
+/*
  * attn_fwd_f32 -- the same fused forward for float32 inputs and output.
  * Same arguments and semantics as attn_fwd, with float32 q, k, v, o.  All
  * arithmetic is fp32 (no rounding of P).

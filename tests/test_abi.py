@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["attn_fwd", "attn_fwd_f32", "attn_materialized",
                             "attn_materialized_workspace_bytes", "attn_strerror",
-                            "attn_abi_version"])
+                            "attn_abi_version", "attn_fwd_select_kernel"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     for st in range(-8, 1):
         assert lib.attn_strerror(st)
     assert lib.attn_strerror(-99) == b"unknown status"
@@ -107,3 +107,14 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), fn
                 assert "attn_oracle" not in text, fn
+
+
+def test_select_kernel_validates_and_returns_previous(lib):
+    """Setting the bf16 kernel choice launches nothing (safe without a GPU)."""
+    assert lib.attn_fwd_select_kernel(7) == -3
+    assert lib.attn_fwd_select_kernel(-1) == -3
+    prev = lib.attn_fwd_select_kernel(api.ATTN_KERNEL_FOURWAVE)
+    assert prev == api.ATTN_KERNEL_AUTO
+    assert lib.attn_fwd_select_kernel(api.ATTN_KERNEL_PINGPONG) == api.ATTN_KERNEL_FOURWAVE
+    assert api.attn_fwd_select_kernel(api.ATTN_KERNEL_AUTO) == api.ATTN_KERNEL_PINGPONG
+

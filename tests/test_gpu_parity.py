@@ -34,6 +34,17 @@ def _gpu():
     api.load_library()
 
 
+@pytest.fixture(params=["pingpong", "fourwave"])
+def bf16_kernel(request):
+    """Run a bf16 test on each of the two forward kernels (forced, not auto-picked)."""
+    which = {"pingpong": api.ATTN_KERNEL_PINGPONG,
+             "fourwave": api.ATTN_KERNEL_FOURWAVE}[request.param]
+    prev = api.attn_fwd_select_kernel(which)
+    _say(f"[parity] bf16 kernel: {request.param}")
+    yield request.param
+    api.attn_fwd_select_kernel(prev)
+
+
 def _dev(x, dtype):
     t = torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
     return t.to(torch.bfloat16) if dtype == "bf16" else t.float()
@@ -75,46 +86,46 @@ EDGE_N = [1, 3, 63, 64, 65, 127, 128, 129, 200, 257]
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", EDGE_N)
-def test_fused_bf16_square(N, causal, D):
+def test_fused_bf16_square(N, causal, D, bf16_kernel):
     _case("fused", 1, 2, N, N, D, causal, seed=N + D)
 
 
 @pytest.mark.parametrize("Nq,Nk", [(64, 200), (200, 64), (129, 1000), (1, 300), (300, 1)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fused_bf16_rectangular(Nq, Nk, causal):
+def test_fused_bf16_rectangular(Nq, Nk, causal, bf16_kernel):
     _case("fused", 2, 1, Nq, Nk, 128, causal, seed=Nq * 7 + Nk)
 
 
 @pytest.mark.parametrize("lens", [[0, 1], [63, 64], [65, 300], [300, 1000], [-3, 999]])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
-def test_fused_bf16_kv_lens(lens, causal, D):
+def test_fused_bf16_kv_lens(lens, causal, D, bf16_kernel):
     """kv_len in {0, 1, BC-1, BC, BC+1, Nk, > Nk, < 0}; with causal, tiles that are
     fully masked for some rows of a wave (later tiles) and for whole waves."""
     _case("fused", 2, 2, 300, 300, D, causal, lens=lens, seed=sum(map(abs, lens)) + D)
 
 
-def test_fused_bf16_beyond_4096_keys():
+def test_fused_bf16_beyond_4096_keys(bf16_kernel):
     """More than 4096 keys per row (page 'Attention softmax fusion', 'Things that
     break': a stack allocation that dies at 4096 columns), odd length."""
     _case("fused", 1, 2, 130, 4097, 128, False, seed=4097)
     _case("fused", 1, 1, 4099, 4099, 64, True, seed=4099)
 
 
-def test_fused_bf16_large_scores():
+def test_fused_bf16_large_scores(bf16_kernel):
     """Score magnitudes of several tens: exponent range and the max subtraction."""
     _case("fused", 1, 2, 256, 256, 128, False, seed=7, std=2.5)
     _case("fused", 1, 2, 256, 256, 64, True, seed=8, std=2.5)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.2, 1e-3, 1.0])
-def test_fused_bf16_scale_values(scale):
+def test_fused_bf16_scale_values(scale, bf16_kernel):
     """scale <= 0 takes the pre-scaled path; tiny and unit scales the normal one."""
     _case("fused", 1, 2, 150, 150, 64, True, seed=11, scale=scale)
     _case("fused", 1, 1, 150, 190, 128, False, lens=[170], seed=12, scale=scale)
 
 
-def test_fused_bf16_rising_max():
+def test_fused_bf16_rising_max(bf16_kernel):
     """Keys that drift along one direction (the long-context recipe, stronger drift so
     a short sequence shows it): the running max rises on most tiles and the output
     must still match."""
@@ -154,7 +165,7 @@ def test_materialized_bf16(causal, lens, D):
 # metamorphic and robustness checks on the GPU output itself
 # ---------------------------------------------------------------------------
 
-def test_deterministic():
+def test_deterministic(bf16_kernel):
     q, k, v, _ = random_case(3, 2, 4, 700, 700, 128)
     qd, kd, vd = (_dev(x, "bf16") for x in (q, k, v))
     _say("[gpu] determinism 2x4x700x128 causal")
@@ -164,7 +175,7 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_keys_beyond_kv_len_are_never_read():
+def test_keys_beyond_kv_len_are_never_read(bf16_kernel):
     """Keys and values at or after kv_len (even NaN) change nothing, bit for bit."""
     q, k, v, _ = random_case(4, 2, 2, 300, 300, 128)
     lens = np.array([130, 257], np.int32)
@@ -181,6 +192,28 @@ def test_keys_beyond_kv_len_are_never_read():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("B,H,N,D,causal,lens", [
+    (1, 2, 300, 128, True, None), (2, 2, 333, 64, False, [0, 200]),
+    (2, 3, 513, 128, False, [512, 7]), (1, 1, 1000, 64, True, None)])
+def test_both_kernels_bitwise_equal(B, H, N, D, causal, lens):
+    """The two bf16 kernels run the same per-wave arithmetic in the same order, so
+    their outputs are identical bit for bit."""
+    q, k, v, lens = random_case(N + D, B, H, N, N, D, "bf16", lens)
+    qd, kd, vd = (_dev(x, "bf16") for x in (q, k, v))
+    ld = _lens_dev(lens)
+    out = {}
+    for which in (api.ATTN_KERNEL_PINGPONG, api.ATTN_KERNEL_FOURWAVE):
+        prev = api.attn_fwd_select_kernel(which)
+        try:
+            _say(f"[gpu] kernel {which} {B}x{H}x{N}x{D} causal={causal} lens={lens}")
+            out[which] = api.attn_fwd(qd, kd, vd, causal=causal, kv_lens=ld)
+            torch.cuda.synchronize()
+        finally:
+            api.attn_fwd_select_kernel(prev)
+    (o1, l1), (o2, l2) = out.values()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_key_permutation_invariance():
     """Without a causal mask, permuting (k_j, v_j) jointly changes O only by rounding."""
     q, k, v, _ = random_case(5, 1, 2, 256, 512, 128)
@@ -192,7 +225,7 @@ def test_key_permutation_invariance():
     assert np.max(np.abs(l1 - l2)) <= 1e-3 * max(1.0, np.abs(l1).max())
 
 
-def test_no_write_outside_outputs():
+def test_no_write_outside_outputs(bf16_kernel):
     """Guard regions around o and lse keep their canary bytes (no out-of-bounds store)."""
     B, H, N, D = 1, 3, 190, 128
     q, k, v, _ = random_case(6, B, H, N, N, D)
