@@ -1,6 +1,7 @@
 """Throughput of the fused attention forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --op softmax_rows      (the standalone row softmax instead)
 
 A step is one call of attn_fwd (the whole fused forward, one kernel launch) on the
 seeded synthetic inputs of a workload, already resident in device memory.  W
@@ -15,6 +16,10 @@ Prints ONE JSON line:
   reported only if it was taken on the current kernel source (else null)
 * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
   workload on this host, in the same unit.
+
+``--op softmax_rows`` times the row softmax (fp32, 8192 x 8192) instead: value in
+GB/s of one read + one write per element, roofline against 8 TB/s of HBM, the
+unfused four-pass baseline's time in ``config``.
 """
 
 import argparse
@@ -84,6 +89,105 @@ def cpu_baseline(w, q, k, v, lens, budget_s):
                       f"metric"}
 
 
+SOFTMAX_ROWS, SOFTMAX_COLS, SOFTMAX_SEED = 8192, 8192, 6
+PEAK_HBM_GBS = 8000.0
+
+
+def softmax_traffic():
+    """Fused row-softmax HBM bytes per launch at 8192 x 8192 from the committed profile."""
+    path = os.path.join(ROOT, "profiles", "traffic_softmax_rows_fused_vs_unfused.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    from exact_attention_89_amd.traffic import _softmax_hash
+    if rec.get("kernel_source_hash") != _softmax_hash():
+        return None
+    for e in rec.get("entries", []):
+        if e["rows"] == SOFTMAX_ROWS and e["cols"] == SOFTMAX_COLS:
+            return e["fused"]["read_bytes"] + e["fused"]["write_bytes"]
+    return None
+
+
+def softmax_cpu_baseline(x, budget_s):
+    """Time the fp64 row-softmax oracle on whole rows of the input until budget_s."""
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    rows, chunk = 0, 64
+    t0 = time.perf_counter()
+    while rows < x.shape[0] and time.perf_counter() - t0 < budget_s:
+        oracle.softmax_rows(x[rows:rows + chunk])
+        rows += chunk
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * rows * x.shape[1] * 4 / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} of {x.shape[0]} rows of the {x.shape[0]}x{x.shape[1]} fp32 input, "
+                      f"fp64 numpy oracle, {dt:.1f} s wall; bytes counted as in the metric"}
+
+
+def bench_softmax(args):
+    """Row softmax (fp32, 8192 x 8192): fused kernel, with the unfused four-pass one beside it."""
+    import numpy as np
+    import torch
+
+    from exact_attention_89_amd import api
+    api.load_library()
+    rng = np.random.default_rng(SOFTMAX_SEED)
+    x = (rng.standard_normal((SOFTMAX_ROWS, SOFTMAX_COLS), dtype=np.float32) * 3.0)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    ws = torch.empty(api.load_library().softmax_rows_unfused_workspace_bytes(SOFTMAX_ROWS),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    algo = 2.0 * SOFTMAX_ROWS * SOFTMAX_COLS * 4
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for s, e in ev:
+            s.record(stream)
+            fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        total = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+        launch = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+        return total, launch
+
+    fused_ms, fused_launch = timed(lambda: api.softmax_rows(xd, out=y))
+    ref_rows = [0, SOFTMAX_ROWS // 2, SOFTMAX_ROWS - 1]
+    got = y[ref_rows].cpu().numpy()
+    unf_ms, _ = timed(lambda: api.softmax_rows_unfused(xd, out=y, workspace=ws))
+    assert not np.isnan(got).any()
+    log(f"[bench] softmax_rows {SOFTMAX_ROWS}x{SOFTMAX_COLS}: fused {fused_ms:.4f} ms, "
+        f"unfused {unf_ms:.4f} ms")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = softmax_cpu_baseline(x, args.cpu_seconds)
+    value = algo / (fused_ms * 1e-3) / 1e9
+    achieved = algo / (fused_launch * 1e-3) / 1e9
+    line = {
+        "metric": "row softmax GB/s (fp32, 8192 rows x 8192 cols, one read + one write)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(fused_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"softmax_rows_{SOFTMAX_ROWS}x{SOFTMAX_COLS}_f32",
+                   "rows": SOFTMAX_ROWS, "cols": SOFTMAX_COLS, "seed": SOFTMAX_SEED,
+                   "unfused_ms_per_step": round(unf_ms, 5),
+                   "unfused_gbs": round(algo / (unf_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": softmax_traffic()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,12 +196,21 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--op", choices=["attention", "softmax_rows"], default="attention",
+                    help="attention: the fused attention forward (default); softmax_rows: "
+                         "the standalone row softmax")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the fused "
               "forward shards by (batch, head) with no communication, so a multi-GPU figure "
               "would be N independent copies of this one", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "softmax_rows":
+        if not os.path.exists(os.path.join(ROOT, "exact_attention_89_amd", "libattn89.so")):
+            from exact_attention_89_amd import build
+            build.build()
+        return bench_softmax(args)
 
     import numpy as np
     import torch

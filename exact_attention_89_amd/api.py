@@ -43,6 +43,9 @@ EXPORTS = {
                                _P]),
     "attn_strerror": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
+    "softmax_rows_f32": (_I, [_P, _P, _I, _I, _P]),
+    "softmax_rows_unfused_workspace_bytes": (_SZ, [_I]),
+    "softmax_rows_unfused_f32": (_I, [_P, _P, _I, _I, _P, _SZ, _P]),
 }
 
 
@@ -175,6 +178,47 @@ def attn_materialized(q, k, v, scale: Optional[float] = None, causal: bool = Fal
                                _stream_handle(torch, q.device))
     _check(st, "attn_materialized")
     return o, l
+
+
+def _rows_prep(x, out):
+    import torch
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a CUDA (HIP) tensor")
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    if x.dim() < 1:
+        raise ValueError("x needs at least one dimension")
+    x = x.contiguous()
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != torch.float32 or not y.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like x")
+    return torch, x, y, rows, cols
+
+
+def softmax_rows(x, out=None):
+    """Row softmax along the last dimension, fp32, fused kernel (one launch)."""
+    torch, x, y, rows, cols = _rows_prep(x, out)
+    st = load_library().softmax_rows_f32(x.data_ptr(), y.data_ptr(), rows, cols,
+                                         _stream_handle(torch, x.device))
+    _check(st, "softmax_rows_f32")
+    return y
+
+
+def softmax_rows_unfused(x, out=None, workspace=None):
+    """Row softmax along the last dimension, fp32, the unfused four-launch baseline."""
+    torch, x, y, rows, cols = _rows_prep(x, out)
+    lib = load_library()
+    need = int(lib.softmax_rows_unfused_workspace_bytes(rows))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    st = lib.softmax_rows_unfused_f32(x.data_ptr(), y.data_ptr(), rows, cols,
+                                      workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream_handle(torch, x.device))
+    _check(st, "softmax_rows_unfused_f32")
+    return y
 
 
 def torch_bf16():

@@ -1,24 +1,31 @@
-"""Device-memory traffic of the fused kernel against the materialised baseline.
+"""Device-memory traffic of the fused kernels against their unfused baselines.
 
-Two subcommands.  ``run`` launches one path on synthetic inputs for several
-sequence lengths, in a fixed order, and writes a manifest of the dispatches it
-made; it is meant to run under ``rocprofv3 --pmc FETCH_SIZE`` (then, in its own
-run, ``WRITE_SIZE``):
+Two kinds of subcommands.  ``run`` launches one path on synthetic inputs over a
+sweep of sizes, in a fixed order, and writes a manifest of the dispatches it made;
+it is meant to run under ``rocprofv3 --pmc FETCH_SIZE`` (then, in its own run,
+``WRITE_SIZE``), with ``--kernel-include-regex 'MulFunctor|attn89'``:
 
-    rocprofv3 --pmc FETCH_SIZE --kernel-include-regex attn89 -d OUT -o fetch \
-        --output-format csv -- python3 -m exact_attention_89_amd.traffic run \
-        --impl fused --N 1024 2048 ... --manifest OUT/manifest.json
+    rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'MulFunctor|attn89' -d OUT \\
+        -o fetch --output-format csv -- python3 -m exact_attention_89_amd.traffic \\
+        run --impl fused --N 1024 2048 ... --manifest OUT/manifest.json
 
-``--impl copy`` launches a plain elementwise kernel of known size (read S bytes,
-write S bytes) to calibrate what the two counters report.  ``summarize`` joins
-the counter CSVs with the manifests and writes a JSON record and a Markdown table.
+Every run first launches a plain elementwise copy (torch.mul, the only MulFunctor
+dispatches of the run) of a known size, so the counters are calibrated against
+bytes that are known, in the same process on the same GPU: how many bytes one
+FETCH_SIZE unit stands for has differed between runs.  ``summarize`` and
+``summarize-softmax`` join the counter CSVs with the manifests and write a JSON
+record and a Markdown table.
 
-The claim being measured (page "Attention softmax fusion", sections "What fused
-has to mean" and "Things that break"; page "Kernel Fusion and the Memory Wall",
-section "FlashAttention: avoid the full score matrix"): the materialised
-pipeline moves Θ(N²) bytes per head through device memory, the fused kernel's
-traffic stays O(N·D) per query block and shows no score-sized term; a single
-short length would hide the difference, so lengths are swept.
+The claims being measured:
+* fused attention (page "Attention softmax fusion", sections "What fused has to
+  mean" and "Things that break"; page "Kernel Fusion and the Memory Wall", section
+  "FlashAttention: avoid the full score matrix"): the materialised pipeline moves
+  Theta(N^2) bytes per head through device memory, the fused kernel's traffic stays
+  O(N D) per query block and shows no score-sized term; a single short length would
+  hide the difference, so lengths are swept;
+* row softmax (page "Kernel Fusion and the Memory Wall", section "Softmax needs a
+  global row statistic"): four reads and two writes per row unfused, one read and
+  one write fused while the row fits on chip.
 """
 
 from __future__ import annotations
@@ -33,15 +40,40 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+KERNEL_REGEX = "MulFunctor|attn89"
 
 
-def _kernel_hash():
+def _hash(files):
     h = hashlib.sha256()
-    for fn in ("attn_fwd_bf16_pp.hip", "attn_fwd_bf16_4w.hip", "attn_bf16_tiles.hpp",
-               "common.hpp"):
+    for fn in files:
         with open(os.path.join(HERE, "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def _kernel_hash():
+    """Sources of the bf16 fused attention kernels."""
+    return _hash(("attn_fwd_bf16_pp.hip", "attn_fwd_bf16_4w.hip", "attn_bf16_tiles.hpp",
+                  "common.hpp"))
+
+
+def _softmax_hash():
+    """Sources of the row-softmax kernels."""
+    return _hash(("softmax_rows.hip", "common.hpp"))
+
+
+def _calibrate(torch, dev, mib, calls):
+    n = mib * (1 << 20) // 4
+    x = torch.empty(n, dtype=torch.float32, device=dev).normal_()
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    print(f"[traffic] calibration copy {mib} MiB x {calls}", flush=True)
+    for _ in range(calls):
+        torch.mul(x, 2.0, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bytes_read": n * 4, "bytes_written": n * 4, "dispatches": calls}
 
 
 def cmd_run(a):
@@ -51,17 +83,27 @@ def cmd_run(a):
     api.load_library()
     dev = torch.device("cuda:0")
     torch.manual_seed(0)
-    manifest = {"impl": a.label or a.impl, "calls": a.calls, "entries": []}
-    if a.impl == "copy":
-        n = a.copy_mib * (1 << 20) // 4
-        x = torch.ones(n, dtype=torch.float32, device=dev)
-        y = torch.empty_like(x)
-        torch.cuda.synchronize()
-        for _ in range(a.calls):
-            torch.mul(x, 2.0, out=y)
-        torch.cuda.synchronize()
-        manifest["entries"].append({"bytes_read": n * 4, "bytes_written": n * 4,
-                                    "dispatches_per_call": 1})
+    manifest = {"impl": a.label or a.impl, "calls": a.calls, "entries": [],
+                "calibration": _calibrate(torch, dev, a.copy_mib, a.calls)}
+    if a.impl in ("softmax_fused", "softmax_unfused"):
+        fn = api.softmax_rows if a.impl == "softmax_fused" else api.softmax_rows_unfused
+        for cols in a.cols:
+            rows = max(1, a.softmax_elems // cols)
+            x = torch.empty(rows, cols, device=dev).normal_(0.0, 3.0)
+            y = torch.empty_like(x)
+            torch.cuda.synchronize()
+            print(f"[traffic] {a.impl} rows={rows} cols={cols}", flush=True)
+            for _ in range(a.calls):
+                fn(x, out=y)
+            torch.cuda.synchronize()
+            manifest["entries"].append({
+                "rows": rows, "cols": cols,
+                "dispatches_per_call": 1 if a.impl == "softmax_fused" else 4,
+                "algorithmic_bytes": 2 * rows * cols * 4,
+            })
+            del x, y
+            torch.cuda.empty_cache()
+        manifest["kernel_source_hash"] = _softmax_hash()
     else:
         for N in a.N:
             for causal in a.causal:
@@ -84,16 +126,15 @@ def cmd_run(a):
                         api.attn_materialized(q, k, v, causal=bool(causal), workspace=ws,
                                               out=o, lse=lse)
                 torch.cuda.synchronize()
-                elt = 2
                 manifest["entries"].append({
                     "N": N, "causal": causal, "B": a.B, "H": a.H, "D": a.D,
                     "dispatches_per_call": 1 if a.impl == "fused" else 3,
-                    "algorithmic_bytes": a.B * a.H * N * a.D * elt * 4 + a.B * a.H * N * 4,
+                    "algorithmic_bytes": a.B * a.H * N * a.D * 2 * 4 + a.B * a.H * N * 4,
                     "one_score_matrix_16bit_all_heads": a.B * a.H * N * N * 2,
                 })
                 del q, k, v, o, lse, ws
                 torch.cuda.empty_cache()
-    manifest["kernel_source_hash"] = _kernel_hash()
+        manifest["kernel_source_hash"] = _kernel_hash()
     with open(a.manifest, "w") as f:
         json.dump(manifest, f, indent=1)
 
@@ -115,88 +156,121 @@ def _read_counters(path_glob):
     return [(name, val * 1024.0) for (did, name), val in sorted(out.items())]  # KiB -> B
 
 
+def _load_run(dirpath, impl):
+    """Manifest, calibration factors and per-call calibrated bytes of one run."""
+    man = json.load(open(os.path.join(dirpath, impl, "manifest.json")))
+    fetch = _read_counters(os.path.join(dirpath, impl, "fetch", "**", "*counter_collection*.csv"))
+    write = _read_counters(os.path.join(dirpath, impl, "write", "**", "*counter_collection*.csv"))
+    cal = man["calibration"]
+    nc = cal["dispatches"]
+    if not all("MulFunctor" in n for n, _ in fetch[:nc] + write[:nc]):
+        raise SystemExit(f"{impl}: the first {nc} dispatches are not the calibration copy")
+    ff = cal["bytes_read"] * nc / sum(v for _, v in fetch[:nc])
+    wf = cal["bytes_written"] * nc / sum(v for _, v in write[:nc])
+    fetch, write = fetch[nc:], write[nc:]
+    entries, pos = [], 0
+    for e in man["entries"]:
+        n = e["dispatches_per_call"] * man["calls"]
+        fsl, wsl = fetch[pos:pos + n], write[pos:pos + n]
+        pos += n
+        kern = {}
+        for (nm, fv), (_, wv) in zip(fsl, wsl):
+            kk = kern.setdefault(nm, [0.0, 0.0])
+            kk[0] += fv * ff / man["calls"]
+            kk[1] += wv * wf / man["calls"]
+        entries.append(dict(e, read_bytes=sum(v for _, v in fsl) * ff / man["calls"],
+                            write_bytes=sum(v for _, v in wsl) * wf / man["calls"],
+                            per_kernel=kern))
+    return man, {"fetch_factor": ff, "write_factor": wf}, entries
+
+
 def cmd_summarize(a):
-    res = {}
-    for impl in ("copy", "fused", "materialized", "headline"):
-        mpath = os.path.join(a.dir, impl, "manifest.json")
-        if not os.path.exists(mpath):
-            continue
-        man = json.load(open(mpath))
-        fetch = _read_counters(os.path.join(a.dir, impl, "fetch", "**", "*counter_collection*.csv"))
-        write = _read_counters(os.path.join(a.dir, impl, "write", "**", "*counter_collection*.csv"))
-        if impl == "copy":
-            fetch, write = fetch[-man["calls"]:], write[-man["calls"]:]
-        entries = []
-        pos = 0
-        for e in man["entries"]:
-            n = e["dispatches_per_call"] * man["calls"]
-            fsl, wsl = fetch[pos:pos + n], write[pos:pos + n]
-            pos += n
-            per_call_f = sum(v for _, v in fsl) / man["calls"]
-            per_call_w = sum(v for _, v in wsl) / man["calls"]
-            kern = {}
-            for (nm, fv), (_, wv) in zip(fsl, wsl):
-                kk = kern.setdefault(nm, [0.0, 0.0])
-                kk[0] += fv / man["calls"]
-                kk[1] += wv / man["calls"]
-            e = dict(e, fetch_bytes=per_call_f, write_bytes=per_call_w, per_kernel=kern)
-            entries.append(e)
-        res[impl] = {"entries": entries, "kernel_source_hash": man.get("kernel_source_hash")}
-    cal = None
-    if "copy" in res:
-        c = res["copy"]["entries"][0]
-        cal = {"fetch_factor": c["bytes_read"] / c["fetch_bytes"],
-               "write_factor": c["bytes_written"] / c["write_bytes"]}
-    res["calibration"] = cal
-    res["commands"] = a.command or []
-    if a.headline_json and "headline" in res and cal:
+    """Fused attention against the materialised baseline, plus the headline record."""
+    res = {"commands": a.command or []}
+    for impl in ("fused", "materialized", "headline"):
+        if os.path.exists(os.path.join(a.dir, impl, "manifest.json")):
+            man, cal, entries = _load_run(a.dir, impl)
+            res[impl] = {"entries": entries, "calibration": cal,
+                         "kernel_source_hash": man.get("kernel_source_hash")}
+    if a.headline_json and "headline" in res:
         e = res["headline"]["entries"][0]
-        rd = e["fetch_bytes"] * cal["fetch_factor"]
-        wr = e["write_bytes"] * cal["write_factor"]
         rec = {"workload": a.headline_name,
-               "fused": {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+               "fused": {"bytes_per_launch": e["read_bytes"] + e["write_bytes"],
+                         "read_bytes": e["read_bytes"], "write_bytes": e["write_bytes"],
                          "algorithmic_bytes": e["algorithmic_bytes"],
                          "kernel_source_hash": res["headline"]["kernel_source_hash"]},
-               "calibration": cal, "commands": a.command or []}
+               "calibration": res["headline"]["calibration"], "commands": a.command or []}
         with open(a.headline_json, "w") as f:
             json.dump(rec, f, indent=1)
-        print(f"headline: read {rd / 2**20:.1f} MiB, write {wr / 2**20:.1f} MiB per launch "
-              f"(algorithmic {e['algorithmic_bytes'] / 2**20:.1f} MiB)")
+        print(f"headline: read {e['read_bytes'] / 2**20:.1f} MiB, write "
+              f"{e['write_bytes'] / 2**20:.1f} MiB per launch (algorithmic "
+              f"{e['algorithmic_bytes'] / 2**20:.1f} MiB)")
     with open(a.out_json, "w") as f:
         json.dump(res, f, indent=1)
-    # Markdown table
     lines = ["# Device-memory traffic: fused kernel vs materialised 3-launch baseline", ""]
-    for c in a.command or []:
-        lines.append(f"    {c}")
+    lines += [f"    {c}" for c in a.command or []]
     lines.append("")
-    if cal:
-        lines.append(f"Calibration (plain elementwise kernel, known bytes): FETCH_SIZE x "
-                     f"{cal['fetch_factor']:.3f}, WRITE_SIZE x {cal['write_factor']:.3f} "
-                     "= true bytes.  Figures below are calibrated.")
-        lines.append("")
-    lines.append("| N | causal | fused read MiB | fused write MiB | algorithmic MiB | "
-                 "materialised read MiB | materialised write MiB | one score matrix (16-bit, "
-                 "all heads) MiB | materialised / fused |")
-    lines.append("|---|---|---|---|---|---|---|---|---|")
-    ff = cal["fetch_factor"] if cal else 1.0
-    wf = cal["write_factor"] if cal else 1.0
+    for impl in ("fused", "materialized", "headline"):
+        if impl in res:
+            c = res[impl]["calibration"]
+            lines.append(f"* calibration of the {impl} run (1 GiB copy in the same process): "
+                         f"FETCH_SIZE x {c['fetch_factor']:.3f}, WRITE_SIZE x "
+                         f"{c['write_factor']:.3f} = true bytes")
+    lines += ["", "Figures below are calibrated.", "",
+              "| N | causal | fused read MiB | fused write MiB | algorithmic MiB | materialised "
+              "read MiB | materialised write MiB | one score matrix (16-bit, all heads) MiB | "
+              "materialised / fused |", "|---|---|---|---|---|---|---|---|---|"]
     fused = {(e["N"], e["causal"]): e for e in res.get("fused", {}).get("entries", [])}
     mat = {(e["N"], e["causal"]): e for e in res.get("materialized", {}).get("entries", [])}
+    mib = float(1 << 20)
+    nan = float("nan")
     for key in sorted(set(fused) | set(mat)):
-        f = fused.get(key)
-        m = mat.get(key)
-        mib = 1 << 20
-        fr = f["fetch_bytes"] * ff / mib if f else float("nan")
-        fw = f["write_bytes"] * wf / mib if f else float("nan")
-        mr = m["fetch_bytes"] * ff / mib if m else float("nan")
-        mw = m["write_bytes"] * wf / mib if m else float("nan")
-        alg = (f or m)["algorithmic_bytes"] / mib
-        sm = (f or m)["one_score_matrix_16bit_all_heads"] / mib
-        ratio = (mr + mw) / (fr + fw) if f and m else float("nan")
-        lines.append(f"| {key[0]} | {key[1]} | {fr:.1f} | {fw:.1f} | {alg:.1f} | {mr:.1f} | "
-                     f"{mw:.1f} | {sm:.1f} | {ratio:.1f} |")
+        f, m = fused.get(key), mat.get(key)
+        fr, fw = (f["read_bytes"] / mib, f["write_bytes"] / mib) if f else (nan, nan)
+        mr, mw = (m["read_bytes"] / mib, m["write_bytes"] / mib) if m else (nan, nan)
+        base = f or m
+        ratio = (mr + mw) / (fr + fw) if f and m else nan
+        lines.append(f"| {key[0]} | {key[1]} | {fr:.1f} | {fw:.1f} | "
+                     f"{base['algorithmic_bytes'] / mib:.1f} | {mr:.1f} | {mw:.1f} | "
+                     f"{base['one_score_matrix_16bit_all_heads'] / mib:.1f} | {ratio:.1f} |")
     with open(a.out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_summarize_softmax(a):
+    """Fused row softmax against the unfused four-pass baseline."""
+    fman, fcal, fused = _load_run(a.dir, "softmax_fused")
+    _, ucal, unf = _load_run(a.dir, "softmax_unfused")
+    rec = {"calibration": {"fused_run": fcal, "unfused_run": ucal},
+           "kernel_source_hash": fman.get("kernel_source_hash"), "commands": a.command or [],
+           "entries": []}
+    lines = ["# Device-memory traffic: fused row softmax vs the unfused four-pass baseline", ""]
+    lines += [f"    {c}" for c in a.command or []]
+    lines += ["", f"Calibration (1 GiB copy in the same process): fused run FETCH_SIZE x "
+              f"{fcal['fetch_factor']:.3f}, WRITE_SIZE x {fcal['write_factor']:.3f}; unfused run "
+              f"FETCH_SIZE x {ucal['fetch_factor']:.3f}, WRITE_SIZE x {ucal['write_factor']:.3f}.  "
+              "fp32, rows x cols = 64 Mi elements (256 MiB) per case.", "",
+              "| rows | cols | algorithmic MiB (1 read + 1 write) | fused read MiB | fused write MiB "
+              "| unfused read MiB | unfused write MiB | unfused / fused |",
+              "|---|---|---|---|---|---|---|---|"]
+    mib = float(1 << 20)
+    for f, u in zip(fused, unf):
+        rec["entries"].append({"rows": f["rows"], "cols": f["cols"],
+                               "algorithmic_bytes": f["algorithmic_bytes"],
+                               "fused": {"read_bytes": f["read_bytes"],
+                                         "write_bytes": f["write_bytes"]},
+                               "unfused": {"read_bytes": u["read_bytes"],
+                                           "write_bytes": u["write_bytes"]}})
+        ratio = (u["read_bytes"] + u["write_bytes"]) / (f["read_bytes"] + f["write_bytes"])
+        lines.append(f"| {f['rows']} | {f['cols']} | {f['algorithmic_bytes'] / mib:.1f} | "
+                     f"{f['read_bytes'] / mib:.1f} | {f['write_bytes'] / mib:.1f} | "
+                     f"{u['read_bytes'] / mib:.1f} | {u['write_bytes'] / mib:.1f} | "
+                     f"{ratio:.2f} |")
+    with open(a.out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(a.out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -204,7 +278,8 @@ def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--impl", choices=["fused", "materialized", "copy"], required=True)
+    r.add_argument("--impl", choices=["fused", "materialized", "softmax_fused",
+                                      "softmax_unfused"], required=True)
     r.add_argument("--label", default=None, help="manifest label (e.g. headline)")
     r.add_argument("--N", type=int, nargs="+", default=[1024, 2048, 4096, 8192, 16384, 32768])
     r.add_argument("--causal", type=int, nargs="+", default=[1, 0])
@@ -213,6 +288,10 @@ def main():
     r.add_argument("--D", type=int, default=128)
     r.add_argument("--calls", type=int, default=2)
     r.add_argument("--copy-mib", type=int, default=1024)
+    r.add_argument("--cols", type=int, nargs="+", default=[1024, 4096, 8192, 16384, 65536],
+                   help="row lengths of the softmax sweep")
+    r.add_argument("--softmax-elems", type=int, default=64 << 20,
+                   help="rows * cols of every softmax case (256 MiB of fp32)")
     r.add_argument("--manifest", required=True)
     s = sub.add_parser("summarize")
     s.add_argument("--dir", required=True)
@@ -221,10 +300,16 @@ def main():
     s.add_argument("--command", action="append")
     s.add_argument("--headline-json", default=None)
     s.add_argument("--headline-name", default="bf16_causal_b1h32_n8192_d128")
+    ss = sub.add_parser("summarize-softmax")
+    ss.add_argument("--dir", required=True)
+    ss.add_argument("--out-json", required=True)
+    ss.add_argument("--out-md", required=True)
+    ss.add_argument("--command", action="append")
     a = ap.parse_args()
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
-    {"run": cmd_run, "summarize": cmd_summarize}[a.cmd](a)
+    {"run": cmd_run, "summarize": cmd_summarize,
+     "summarize-softmax": cmd_summarize_softmax}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -8,3 +8,4 @@ from .attn_oracle import (  # noqa: F401
     kv_length,
     valid_keys,
 )
+from .softmax_oracle import softmax_rows, softmax_rows_four_pass  # noqa: F401

@@ -3,6 +3,7 @@ declares, and rejects invalid arguments before launching anything (these calls
 return from host-side checks and never touch a device)."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -11,13 +12,13 @@ import pytest
 from exact_attention_89_amd import api
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:attn|softmax_rows)\w*)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +33,9 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["attn_fwd", "attn_fwd_f32", "attn_materialized",
                             "attn_materialized_workspace_bytes", "attn_strerror",
-                            "attn_abi_version", "attn_fwd_select_kernel"])
+                            "attn_abi_version", "attn_fwd_select_kernel",
+                            "softmax_rows_f32", "softmax_rows_unfused_workspace_bytes",
+                            "softmax_rows_unfused_f32"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -118,3 +121,21 @@ def test_select_kernel_validates_and_returns_previous(lib):
     assert lib.attn_fwd_select_kernel(api.ATTN_KERNEL_PINGPONG) == api.ATTN_KERNEL_FOURWAVE
     assert api.attn_fwd_select_kernel(api.ATTN_KERNEL_AUTO) == api.ATTN_KERNEL_PINGPONG
 
+
+
+def test_softmax_rows_rejects_bad_arguments(lib):
+    """Host-side checks of the row-softmax entry points (nothing is launched)."""
+    p = ctypes.c_void_p(0x10000)          # aligned, never dereferenced
+    odd = ctypes.c_void_p(0x10002)        # not 4-byte aligned
+    assert lib.softmax_rows_f32(None, p, 1, 1, None) == -1
+    assert lib.softmax_rows_f32(p, p, 0, 4, None) == -2
+    assert lib.softmax_rows_f32(p, p, 4, 0, None) == -2
+    assert lib.softmax_rows_f32(p, p, 1, 1 << 30, None) == -8
+    assert lib.softmax_rows_f32(odd, p, 1, 4, None) == -4
+    assert lib.softmax_rows_unfused_workspace_bytes(0) == 0
+    need = lib.softmax_rows_unfused_workspace_bytes(1000)
+    assert need >= 2 * 1000 * 4 and need % 256 == 0
+    assert lib.softmax_rows_unfused_f32(p, p, 1000, 8, p, need - 1, None) == -6
+    assert lib.softmax_rows_unfused_f32(p, p, 1000, 8, None, need, None) == -6
+    assert lib.softmax_rows_unfused_f32(p, p, 1000, 8, ctypes.c_void_p(0x10040), need,
+                                        None) == -6
