@@ -196,9 +196,11 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--op", choices=["attention", "softmax_rows"], default="attention",
-                    help="attention: the fused attention forward (default); softmax_rows: "
-                         "the standalone row softmax")
+    ap.add_argument("--op", choices=["attention", "partial", "materialized", "softmax_rows"],
+                    default="attention",
+                    help="attention: the fused attention forward (default); partial: QK^T + "
+                         "softmax fused, P through device memory, then P V; materialized: the "
+                         "three-launch baseline; softmax_rows: the standalone row softmax")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the fused "
@@ -234,8 +236,28 @@ def main():
     o = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
 
-    def step():
-        api.attn_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, kv_lens=ld, out=o, lse=lse)
+    ldk = (w.Nk + 63) // 64 * 64
+    if args.op == "attention":
+        def step():
+            api.attn_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, kv_lens=ld, out=o, lse=lse)
+        extra_bytes = 0
+    elif args.op == "partial":
+        ws = torch.empty(api.attn_partial_workspace_bytes(w.B, w.H, w.Nq, w.Nk),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            api.attn_partial(qd, kd, vd, scale=w.scale, causal=w.causal, kv_lens=ld,
+                             workspace=ws, out=o, lse=lse)
+        extra_bytes = 2 * 2 * w.B * w.H * w.Nq * ldk            # P written once, read once
+    else:
+        ws = torch.empty(api.attn_materialized_workspace_bytes(w.B, w.H, w.Nq, w.Nk),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            api.attn_materialized(qd, kd, vd, scale=w.scale, causal=w.causal, kv_lens=ld,
+                                  workspace=ws, out=o, lse=lse)
+        # S fp32 written once and read twice, P bf16 written once and read once
+        extra_bytes = (4 + 8 + 2 + 2) * w.B * w.H * w.Nq * ldk
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -269,6 +291,29 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] cpu_baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(w, q, k, v, lens, args.cpu_seconds)
+
+    if args.op != "attention":
+        # multi-launch paths: bound by device memory; bytes = inputs + outputs + the
+        # score-sized tensors the path moves, over the whole call
+        io_bytes = 2 * (2 * w.B * w.H * w.Nq * w.D + 2 * w.B * w.H * w.Nk * w.D) + \
+            4 * w.B * w.H * w.Nq
+        algo_bytes = io_bytes + extra_bytes
+        gbs = algo_bytes / (mean_launch_ms * 1e-3) / 1e9
+        line = {
+            "metric": f"attn fwd TFLOP/s, {args.op} path (B,H,N,D=1,32,8192,128 causal)",
+            "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": name, "op": args.op, "B": w.B, "H": w.H, "Nq": w.Nq,
+                       "Nk": w.Nk, "D": w.D, "causal": w.causal, "seed": w.seed,
+                       "algorithmic_bytes_per_call": algo_bytes},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+            "cpu_baseline": cpu,
+        }
+        print(json.dumps(line), flush=True)
+        return
 
     traffic = measured_traffic(name)
     line = {

@@ -41,6 +41,8 @@ EXPORTS = {
     "attn_materialized_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "attn_materialized": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ,
                                _P]),
+    "attn_partial_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "attn_partial": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ, _P]),
     "attn_strerror": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
     "softmax_rows_f32": (_I, [_P, _P, _I, _I, _P]),
@@ -219,6 +221,31 @@ def softmax_rows_unfused(x, out=None, workspace=None):
                                       _stream_handle(torch, x.device))
     _check(st, "softmax_rows_unfused_f32")
     return y
+
+
+def attn_partial_workspace_bytes(B: int, H: int, Nq: int, Nk: int) -> int:
+    return int(load_library().attn_partial_workspace_bytes(B, H, Nq, Nk))
+
+
+def attn_partial(q, k, v, scale: Optional[float] = None, causal: bool = False,
+                 kv_lens=None, workspace=None, out=None, lse=None):
+    """Partial fusion: QK^T + softmax in one launch writing P, then P V (two launches)."""
+    torch, q, k, v, kv_lens, (B, H, Nq, Nk, D) = _prep(q, k, v, kv_lens, torch_bf16())
+    if scale is None:
+        scale = D ** -0.5
+    lib = load_library()
+    need = int(lib.attn_partial_workspace_bytes(B, H, Nq, Nk))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib.attn_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          l.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                          kv_lens.data_ptr() if kv_lens is not None else None,
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream_handle(torch, q.device))
+    _check(st, "attn_partial")
+    return o, l
 
 
 def torch_bf16():

@@ -146,6 +146,33 @@ int attn_materialized(const void* q, const void* k, const void* v, void* o, floa
   return attn89::launch_attn_materialized(a, D, scale, workspace, lay, (hipStream_t)stream);
 }
 
+size_t attn_partial_workspace_bytes(int B, int H, int Nq, int Nk) {
+  attn89::MatLayout lay;
+  if (!attn89::materialized_layout(B, H, Nq, Nk, &lay)) return 0;
+  const size_t p_bytes = lay.total - lay.p_offset;   // P alone: B*H*Nq*ld*2
+  return (p_bytes + 255) / 256 * 256;
+}
+
+int attn_partial(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int H, int Nq, int Nk, int D, float scale, int causal,
+                 const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, kv_lens, 2);
+  if (st != ATTN_OK) return st;
+  if (((size_t)Nq + 256) * D * 2 >= ((size_t)1 << 31) ||
+      ((size_t)Nk + 256) * D * 2 >= ((size_t)1 << 31))
+    return ATTN_ERR_TOO_LARGE;
+  if ((long long)B * H > 65535) return ATTN_ERR_TOO_LARGE;   // grid of the P V launch
+  attn89::MatLayout lay;
+  if (!attn89::materialized_layout(B, H, Nq, Nk, &lay)) return ATTN_ERR_SHAPE;
+  if (!workspace || workspace_bytes < attn_partial_workspace_bytes(B, H, Nq, Nk) ||
+      !aligned(workspace, 256))
+    return ATTN_ERR_WORKSPACE;
+  attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
+  return attn89::launch_attn_partial(a, D, lay.ld, (unsigned short*)workspace,
+                                     (hipStream_t)stream);
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";

@@ -219,4 +219,15 @@ int launch_attn_materialized(const FwdArgs& a, int D, float scale, void* workspa
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
+int launch_pv(const FwdArgs& a, int D, int ld, const unsigned short* P, hipStream_t stream) {
+  const int BH = a.B * a.H;
+  if (BH > 65535) return -8;
+  const dim3 g3((a.Nq + 127) / 128, BH);
+  if (D == 128)
+    pv_kernel<128><<<g3, 256, 0, stream>>>(a, ld, P);
+  else
+    pv_kernel<64><<<g3, 256, 0, stream>>>(a, ld, P);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
 }  // namespace attn89

@@ -27,4 +27,12 @@ bool materialized_layout(int B, int H, int Nq, int Nk, MatLayout* out);
 int launch_attn_materialized(const FwdArgs& a, int D, float scale, void* workspace,
                              const MatLayout& lay, hipStream_t stream);
 
+// O = P V for a probability matrix P (bf16, [B][H][Nq][ld], every column < ld
+// defined, zeros where masked); the third launch of the materialised baseline.
+int launch_pv(const FwdArgs& a, int D, int ld, const unsigned short* P, hipStream_t stream);
+
+// Partial fusion: QK^T and softmax in one launch writing P (bf16) and LSE, then
+// launch_pv.  P: [B][H][Nq][ld], ld = Nk rounded up to 64.
+int launch_attn_partial(const FwdArgs& a, int D, int ld, unsigned short* P, hipStream_t stream);
+
 }  // namespace attn89

@@ -117,18 +117,24 @@ def cmd_run(a):
                 if a.impl == "materialized":
                     ws = torch.empty(api.attn_materialized_workspace_bytes(a.B, a.H, N, N),
                                      dtype=torch.uint8, device=dev)
+                elif a.impl == "partial":
+                    ws = torch.empty(api.attn_partial_workspace_bytes(a.B, a.H, N, N),
+                                     dtype=torch.uint8, device=dev)
                 torch.cuda.synchronize()
                 print(f"[traffic] {a.impl} N={N} causal={causal}", flush=True)
                 for _ in range(a.calls):
                     if a.impl == "fused":
                         api.attn_fwd(q, k, v, causal=bool(causal), out=o, lse=lse)
+                    elif a.impl == "partial":
+                        api.attn_partial(q, k, v, causal=bool(causal), workspace=ws,
+                                         out=o, lse=lse)
                     else:
                         api.attn_materialized(q, k, v, causal=bool(causal), workspace=ws,
                                               out=o, lse=lse)
                 torch.cuda.synchronize()
                 manifest["entries"].append({
                     "N": N, "causal": causal, "B": a.B, "H": a.H, "D": a.D,
-                    "dispatches_per_call": 1 if a.impl == "fused" else 3,
+                    "dispatches_per_call": {"fused": 1, "partial": 2}.get(a.impl, 3),
                     "algorithmic_bytes": a.B * a.H * N * a.D * 2 * 4 + a.B * a.H * N * 4,
                     "one_score_matrix_16bit_all_heads": a.B * a.H * N * N * 2,
                 })
@@ -187,7 +193,7 @@ def _load_run(dirpath, impl):
 def cmd_summarize(a):
     """Fused attention against the materialised baseline, plus the headline record."""
     res = {"commands": a.command or []}
-    for impl in ("fused", "materialized", "headline"):
+    for impl in ("fused", "partial", "materialized", "headline"):
         if os.path.exists(os.path.join(a.dir, impl, "manifest.json")):
             man, cal, entries = _load_run(a.dir, impl)
             res[impl] = {"entries": entries, "calibration": cal,
@@ -210,29 +216,35 @@ def cmd_summarize(a):
     lines = ["# Device-memory traffic: fused kernel vs materialised 3-launch baseline", ""]
     lines += [f"    {c}" for c in a.command or []]
     lines.append("")
-    for impl in ("fused", "materialized", "headline"):
+    for impl in ("fused", "partial", "materialized", "headline"):
         if impl in res:
             c = res[impl]["calibration"]
             lines.append(f"* calibration of the {impl} run (1 GiB copy in the same process): "
                          f"FETCH_SIZE x {c['fetch_factor']:.3f}, WRITE_SIZE x "
                          f"{c['write_factor']:.3f} = true bytes")
-    lines += ["", "Figures below are calibrated.", "",
-              "| N | causal | fused read MiB | fused write MiB | algorithmic MiB | materialised "
-              "read MiB | materialised write MiB | one score matrix (16-bit, all heads) MiB | "
-              "materialised / fused |", "|---|---|---|---|---|---|---|---|---|"]
-    fused = {(e["N"], e["causal"]): e for e in res.get("fused", {}).get("entries", [])}
-    mat = {(e["N"], e["causal"]): e for e in res.get("materialized", {}).get("entries", [])}
+    lines += ["", "Figures below are calibrated (MiB per call).", "",
+              "| N | causal | algorithmic | one score matrix (16-bit, all heads) | fused read | "
+              "fused write | partial read | partial write | materialised read | materialised "
+              "write | partial / fused | materialised / fused | materialised / partial |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    runs = {impl: {(e["N"], e["causal"]): e for e in res.get(impl, {}).get("entries", [])}
+            for impl in ("fused", "partial", "materialized")}
     mib = float(1 << 20)
     nan = float("nan")
-    for key in sorted(set(fused) | set(mat)):
-        f, m = fused.get(key), mat.get(key)
-        fr, fw = (f["read_bytes"] / mib, f["write_bytes"] / mib) if f else (nan, nan)
-        mr, mw = (m["read_bytes"] / mib, m["write_bytes"] / mib) if m else (nan, nan)
-        base = f or m
-        ratio = (mr + mw) / (fr + fw) if f and m else nan
-        lines.append(f"| {key[0]} | {key[1]} | {fr:.1f} | {fw:.1f} | "
-                     f"{base['algorithmic_bytes'] / mib:.1f} | {mr:.1f} | {mw:.1f} | "
-                     f"{base['one_score_matrix_16bit_all_heads'] / mib:.1f} | {ratio:.1f} |")
+
+    def rw(e):
+        return (e["read_bytes"] / mib, e["write_bytes"] / mib) if e else (nan, nan)
+
+    keys = sorted(set().union(*[set(r) for r in runs.values()]))
+    for key in keys:
+        f, pa, m = (runs[i].get(key) for i in ("fused", "partial", "materialized"))
+        (fr, fw), (pr, pw), (mr, mw) = rw(f), rw(pa), rw(m)
+        base = f or pa or m
+        lines.append(f"| {key[0]} | {key[1]} | {base['algorithmic_bytes'] / mib:.1f} | "
+                     f"{base['one_score_matrix_16bit_all_heads'] / mib:.1f} | {fr:.1f} | "
+                     f"{fw:.1f} | {pr:.1f} | {pw:.1f} | {mr:.1f} | {mw:.1f} | "
+                     f"{(pr + pw) / (fr + fw):.1f} | {(mr + mw) / (fr + fw):.1f} | "
+                     f"{(mr + mw) / (pr + pw):.2f} |")
     with open(a.out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -278,7 +290,7 @@ def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--impl", choices=["fused", "materialized", "softmax_fused",
+    r.add_argument("--impl", choices=["fused", "partial", "materialized", "softmax_fused",
                                       "softmax_unfused"], required=True)
     r.add_argument("--label", default=None, help="manifest label (e.g. headline)")
     r.add_argument("--N", type=int, nargs="+", default=[1024, 2048, 4096, 8192, 16384, 32768])

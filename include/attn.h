@@ -134,6 +134,35 @@ int attn_materialized(const void* q, const void* k, const void* v, void* o, floa
                       const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * attn_partial_workspace_bytes -- bytes of workspace attn_partial needs: the
+ * probability matrix P (bfloat16), B*H*Nq*ld*2 bytes with ld = Nk rounded up to
+ * 64, plus alignment padding.  Returns 0 when a size is < 1 or overflows.
+ */
+size_t attn_partial_workspace_bytes(int B, int H, int Nq, int Nk);
+
+/*
+ * attn_partial -- partial fusion, two launches: Q.K^T and the softmax fused in
+ * one kernel that keeps each score tile in registers through the row maximum,
+ * the exponential and the division, but writes the probabilities P (bfloat16)
+ * to the workspace; then O = P V in a second kernel that reads them back (page
+ * "Attention softmax fusion", section "What fused has to mean": fusing one
+ * boundary leaves a score-sized tensor behind).  The first kernel visits the
+ * key tiles twice (row statistics, then P), so it spends twice the Q.K^T
+ * arithmetic of attn_fwd; masked entries and key tiles no query of a block can
+ * see are written as zeros, so every column below ld is defined.
+ *
+ * Inputs, outputs and mask semantics as attn_fwd (bfloat16); same tolerance.
+ * `workspace`: caller-owned device buffer of at least
+ * attn_partial_workspace_bytes(B, H, Nq, Nk) bytes, 256-byte aligned
+ * (ATTN_ERR_WORKSPACE otherwise); on return it holds P.  B*H must be at most
+ * 65535 (ATTN_ERR_TOO_LARGE).
+ */
+int attn_partial(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                 const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 /* attn_strerror -- a static, NUL-terminated description of a status code. */
 const char* attn_strerror(int status);
 

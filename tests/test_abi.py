@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                             "attn_materialized_workspace_bytes", "attn_strerror",
                             "attn_abi_version", "attn_fwd_select_kernel",
                             "softmax_rows_f32", "softmax_rows_unfused_workspace_bytes",
-                            "softmax_rows_unfused_f32"])
+                            "softmax_rows_unfused_f32", "attn_partial",
+                            "attn_partial_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):

@@ -60,6 +60,8 @@ def _run(impl, q, k, v, scale, causal, lens, dtype):
     if impl == "fused":
         fn = api.attn_fwd if dtype == "bf16" else api.attn_fwd_f32
         o, lse = fn(qd, kd, vd, scale=scale, causal=causal, kv_lens=ld)
+    elif impl == "partial":
+        o, lse = api.attn_partial(qd, kd, vd, scale=scale, causal=causal, kv_lens=ld)
     else:
         o, lse = api.attn_materialized(qd, kd, vd, scale=scale, causal=causal, kv_lens=ld)
     torch.cuda.synchronize()
@@ -164,6 +166,38 @@ def test_materialized_bf16(causal, lens, D):
 # ---------------------------------------------------------------------------
 # metamorphic and robustness checks on the GPU output itself
 # ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 129, 200, 300])
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (False, [0, 77]),
+                                         (True, [150, 1]), (False, [-3, 999])])
+@pytest.mark.parametrize("D", [64, 128])
+def test_partial_bf16(N, causal, lens, D):
+    """Partial fusion (QK^T + softmax fused, P through memory, then P V)."""
+    _case("partial", 2, 2, N, N, D, causal, lens=lens, seed=N * 3 + D)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 1.0])
+def test_partial_bf16_scale_and_rectangular(scale):
+    _case("partial", 1, 2, 150, 333, 128, False, seed=31, scale=scale)
+    _case("partial", 1, 1, 333, 150, 64, True, lens=[120], seed=32, scale=scale)
+
+
+def test_partial_workspace_holds_p():
+    """After attn_partial the workspace holds P: rows sum to 1 over valid keys, zeros
+    elsewhere (causal, so the upper triangle is zero)."""
+    B, H, N, D = 1, 2, 200, 128
+    q, k, v, _ = random_case(41, B, H, N, N, D)
+    qd, kd, vd = (_dev(x, "bf16") for x in (q, k, v))
+    ld = (N + 63) // 64 * 64
+    ws = torch.empty(api.attn_partial_workspace_bytes(B, H, N, N), dtype=torch.uint8,
+                     device="cuda")
+    _say("[gpu] partial workspace P 1x2x200x128 causal")
+    api.attn_partial(qd, kd, vd, causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    P = ws[:B * H * N * ld * 2].view(torch.bfloat16).view(B, H, N, ld).float().cpu().numpy()
+    assert np.all(np.triu(P[0, 0, :, :N], 1) == 0) and np.all(P[..., N:] == 0)
+    assert np.max(np.abs(P.sum(-1) - 1.0)) <= 2e-2
+
 
 def test_deterministic(bf16_kernel):
     q, k, v, _ = random_case(3, 2, 4, 700, 700, 128)
