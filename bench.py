@@ -188,6 +188,84 @@ def bench_softmax(args):
     print(json.dumps(line), flush=True)
 
 
+DECODE = dict(B=1, H=8, Nq=1, Nk=65536, D=128, seed=7)
+
+
+def bench_decode(args):
+    """Split-key decode: one query per head against a 65536-key cache (bf16)."""
+    import numpy as np
+    import torch
+
+    from exact_attention_89_amd import api
+    from exact_attention_89_amd.workloads import round_to_bf16
+    api.load_library()
+    B, H, Nq, Nk, D = (DECODE[k] for k in ("B", "H", "Nq", "Nk", "D"))
+    rng = np.random.default_rng(DECODE["seed"])
+    q, k, v = (round_to_bf16(rng.standard_normal(s, dtype=np.float32))
+               for s in ((B, H, Nq, D), (B, H, Nk, D), (B, H, Nk, D)))
+    qd, kd, vd = (torch.from_numpy(x).cuda().to(torch.bfloat16) for x in (q, k, v))
+    scale = 1.0 / D ** 0.5
+    ws = torch.empty(api.attn_splitkv_workspace_bytes(B, H, Nq, Nk, D, 0), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for s_, e in ev:
+            s_.record(stream)
+            fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        return (ev[0][0].elapsed_time(ev[-1][1]) / args.steps,
+                float(np.mean([s_.elapsed_time(e) for s_, e in ev])))
+
+    split_ms, split_launch = timed(lambda: api.attn_fwd_splitkv(
+        qd, kd, vd, scale=scale, workspace=ws, out=o, lse=lse))
+    assert not torch.isnan(o).any().item()
+    fused_ms, _ = timed(lambda: api.attn_fwd(qd, kd, vd, scale=scale, out=o, lse=lse))
+    kv_bytes = 2.0 * B * H * Nk * D * 2
+    log(f"[bench] decode: splitkv {split_ms:.4f} ms, fused {fused_ms:.4f} ms")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        import oracle
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+        t0, heads = time.perf_counter(), 0
+        for h in range(H):
+            oracle.attention_oracle(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], scale)
+            heads += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": kv_bytes / H * heads / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{heads} of {H} heads, every key, fp64 numpy oracle, {dt:.1f} s wall; "
+                         f"bytes counted as in the metric (K and V read once)"}
+    achieved = kv_bytes / (split_launch * 1e-3) / 1e9
+    line = {
+        "metric": "split-KV decode GB/s of K+V (bf16, B=1 H=8 Nq=1 Nk=65536 D=128)",
+        "value": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(split_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_b1h8_nq1_nk65536_d128", **DECODE,
+                   "num_splits": int(api.load_library().attn_splitkv_num_splits(B, H, Nq, Nk, 0)),
+                   "fused_attn_fwd_ms_per_step": round(fused_ms, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,11 +274,13 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--op", choices=["attention", "partial", "materialized", "softmax_rows"],
+    ap.add_argument("--op", choices=["attention", "partial", "materialized", "softmax_rows",
+                                     "decode"],
                     default="attention",
                     help="attention: the fused attention forward (default); partial: QK^T + "
                          "softmax fused, P through device memory, then P V; materialized: the "
-                         "three-launch baseline; softmax_rows: the standalone row softmax")
+                         "three-launch baseline; softmax_rows: the standalone row softmax; "
+                         "decode: split-key attention for one query against a long cache")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the fused "
@@ -208,11 +288,11 @@ def main():
               "would be N independent copies of this one", file=sys.stderr)
         sys.exit(2)
 
-    if args.op == "softmax_rows":
+    if args.op in ("softmax_rows", "decode"):
         if not os.path.exists(os.path.join(ROOT, "exact_attention_89_amd", "libattn89.so")):
             from exact_attention_89_amd import build
             build.build()
-        return bench_softmax(args)
+        return bench_softmax(args) if args.op == "softmax_rows" else bench_decode(args)
 
     import numpy as np
     import torch

@@ -42,6 +42,10 @@ EXPORTS = {
     "attn_materialized": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ,
                                _P]),
     "attn_partial_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "attn_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "attn_splitkv_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _P, _SZ,
+                              _P]),
     "attn_partial": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ, _P]),
     "attn_strerror": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
@@ -245,6 +249,33 @@ def attn_partial(q, k, v, scale: Optional[float] = None, causal: bool = False,
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream_handle(torch, q.device))
     _check(st, "attn_partial")
+    return o, l
+
+
+def attn_splitkv_workspace_bytes(B: int, H: int, Nq: int, Nk: int, D: int,
+                                 num_splits: int = 0) -> int:
+    return int(load_library().attn_splitkv_workspace_bytes(B, H, Nq, Nk, D, num_splits))
+
+
+def attn_fwd_splitkv(q, k, v, scale: Optional[float] = None, causal: bool = False,
+                     kv_lens=None, num_splits: int = 0, workspace=None, out=None, lse=None):
+    """Fused forward with the keys split across workgroups, then merged (two launches)."""
+    torch, q, k, v, kv_lens, (B, H, Nq, Nk, D) = _prep(q, k, v, kv_lens, torch_bf16())
+    if scale is None:
+        scale = D ** -0.5
+    lib = load_library()
+    need = int(lib.attn_splitkv_workspace_bytes(B, H, Nq, Nk, D, int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              l.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                              kv_lens.data_ptr() if kv_lens is not None else None,
+                              int(num_splits), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(),
+                              _stream_handle(torch, q.device))
+    _check(st, "attn_fwd_splitkv")
     return o, l
 
 

@@ -37,7 +37,7 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
 attn89::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int H, int Nq, int Nk, float scale, int causal,
                           const int32_t* kv_lens) {
-  attn89::FwdArgs a;
+  attn89::FwdArgs a = {};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -80,12 +80,14 @@ int num_cus() {
 }
 
 // The 8-wave ping-pong kernel (one 256-row workgroup per CU) is the faster one once
-// its grid covers every CU; below that, and for D = 64 (where the softmax, not the
-// matrix work, bounds a tile), the 4-wave kernel with twice as many workgroups wins.
+// its blocks are full (Nq >= 256) and its grid covers every CU; below that, and for
+// D = 64 (where the softmax, not the matrix work, bounds a tile), the 4-wave kernel
+// with smaller blocks and twice as many workgroups wins.
 int pick_bf16_kernel(int B, int H, int Nq, int D) {
   if (g_bf16_kernel != ATTN_KERNEL_AUTO) return g_bf16_kernel;
   const long long pp_grid = (long long)((Nq + 255) / 256) * B * H;
-  return (D == 128 && pp_grid >= num_cus()) ? ATTN_KERNEL_PINGPONG : ATTN_KERNEL_FOURWAVE;
+  return (D == 128 && Nq >= 256 && pp_grid >= num_cus()) ? ATTN_KERNEL_PINGPONG
+                                                         : ATTN_KERNEL_FOURWAVE;
 }
 
 }  // namespace
@@ -144,6 +146,57 @@ int attn_materialized(const void* q, const void* k, const void* v, void* o, floa
     return ATTN_ERR_WORKSPACE;
   attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
   return attn89::launch_attn_materialized(a, D, scale, workspace, lay, (hipStream_t)stream);
+}
+
+// workspace of attn_fwd_splitkv: o_part (fp32) then lse_part, each 256-aligned
+static bool splitkv_layout(int B, int H, int Nq, int Nk, int D, int num_splits, int* splits,
+                           int* chunk, size_t* lse_off, size_t* total) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (D != 64 && D != 128)) return false;
+  *splits = attn89::splitkv_plan(B, H, Nq, Nk, num_splits, num_cus(), chunk);
+  size_t rows = 0, o_elems = 0;
+  if (__builtin_mul_overflow((size_t)B * (size_t)H, (size_t)Nq, &rows)) return false;
+  if (__builtin_mul_overflow(rows * (size_t)*splits, (size_t)D, &o_elems)) return false;
+  if (o_elems > ((size_t)1 << 56)) return false;
+  *lse_off = (o_elems * 4 + 255) / 256 * 256;
+  *total = *lse_off + (rows * (size_t)*splits * 4 + 255) / 256 * 256;
+  return true;
+}
+
+int attn_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_splits) {
+  int chunk = 0;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
+  return attn89::splitkv_plan(B, H, Nq, Nk, num_splits, num_cus(), &chunk);
+}
+
+size_t attn_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int D, int num_splits) {
+  int splits = 0, chunk = 0;
+  size_t lse_off = 0, total = 0;
+  if (!splitkv_layout(B, H, Nq, Nk, D, num_splits, &splits, &chunk, &lse_off, &total)) return 0;
+  return total;
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Nq, int Nk, int D, float scale, int causal,
+                     const int32_t* kv_lens, int num_splits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, kv_lens, 2);
+  if (st != ATTN_OK) return st;
+  if (((size_t)Nq + 256) * D * 2 >= ((size_t)1 << 31) ||
+      ((size_t)Nk + 256) * D * 2 >= ((size_t)1 << 31))
+    return ATTN_ERR_TOO_LARGE;
+  int splits = 0, chunk = 0;
+  size_t lse_off = 0, total = 0;
+  if (!splitkv_layout(B, H, Nq, Nk, D, num_splits, &splits, &chunk, &lse_off, &total))
+    return ATTN_ERR_SHAPE;
+  if ((long long)((Nq + 127) / 128) * B * H * splits > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  if (!workspace || workspace_bytes < total || !aligned(workspace, 256))
+    return ATTN_ERR_WORKSPACE;
+  attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
+  a.n_splits = splits;
+  a.kv_chunk = chunk;
+  a.o_part = (float*)workspace;
+  a.lse_part = (float*)((char*)workspace + lse_off);
+  return attn89::launch_attn_splitkv(a, D, (hipStream_t)stream);
 }
 
 size_t attn_partial_workspace_bytes(int B, int H, int Nq, int Nk) {

@@ -67,7 +67,9 @@ struct Cfg {
 
 // PRE: scale <= 0, so scores are scaled before they are masked (a separate
 // instantiation keeps that branch out of the common kernel).
-template <int D, bool PRE>
+// SPLIT: the workgroup covers one key range of the row block and writes a partial
+// result (normalised O_r in fp32 and LSE_r) for the merge of attn_splitkv.hip.
+template <int D, bool PRE, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
@@ -85,8 +87,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   // head lands on the same XCD and its K/V re-reads stay in that XCD's L2.
   const int BH = p.B * p.H;
   const int n_qb = (p.Nq + C::BR - 1) / C::BR;
-  const int qb = n_qb - 1 - (int)blockIdx.x / BH;
-  const int bh = (int)blockIdx.x % BH;
+  const int split = SPLIT ? (int)blockIdx.x % p.n_splits : 0;
+  const int wg_id = SPLIT ? (int)blockIdx.x / p.n_splits : (int)blockIdx.x;
+  const int qb = n_qb - 1 - wg_id / BH;
+  const int bh = wg_id % BH;
   const int b = bh / p.H;
 
   const unsigned short* qp = (const unsigned short*)p.q + (size_t)bh * p.Nq * D;
@@ -99,7 +103,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   const int q0 = qb * C::BR;
   const int q_hi = min(q0 + C::BR, p.Nq);
   const int kv_end = p.causal ? min(L, q_hi) : L;    // keys any row of the block sees
-  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  const int n_tiles_all = (kv_end + C::BC - 1) / C::BC;
+  // key tiles [t_begin, n_tiles) of this workgroup (all of them unless split)
+  const int t_begin = SPLIT ? split * (p.kv_chunk / C::BC) : 0;
+  const int n_tiles = SPLIT ? min(n_tiles_all, t_begin + p.kv_chunk / C::BC) : n_tiles_all;
   const int qw = q0 + wave * 32;                     // first row of this wave
   const int qrow = qw + lq;
 
@@ -290,15 +297,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     }
   };
 
-  // ---- prologue: K(0) and V(0) in LDS ----
-  if (n_tiles > 0) {
-    load_v(0);
-    load_k(0, 0);
+  // ---- prologue: K(t_begin) and V(t_begin) in LDS ----
+  if (n_tiles > t_begin) {
+    load_v(t_begin);
+    load_k(t_begin, 0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
-  if (n_tiles > 0) store_v(0);
+  if (n_tiles > t_begin) store_v(0);
   __syncthreads();
-  int t = 0;
+  int t = t_begin;
   for (; t + 2 < n_tiles; t += 2) {
     iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
     iteration(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
@@ -312,6 +319,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
 
   // ---- epilogue: O = a / l (0 for rows with no valid key), LSE = ln2 (m + log2 l) ----
   const float l_tot = sum_with_partner(l_run);
+  if (SPLIT) {
+    // partial result of this key range, fp32 for the merge (an empty range gives
+    // O_r = 0 and LSE_r = -inf, weight 0 in the merge)
+    if (qrow < p.Nq) {
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      const size_t row = ((size_t)split * BH + bh) * p.Nq + qrow;
+      float* orow = p.o_part + row * D;
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *(f32x4*)(orow + d * 32 + 8 * a + 4 * lg) =
+              (f32x4){oacc[d][4 * a + 0] * inv, oacc[d][4 * a + 1] * inv,
+                      oacc[d][4 * a + 2] * inv, oacc[d][4 * a + 3] * inv};
+      if (lg == 0)
+        p.lse_part[row] = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   if (qrow < p.Nq) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     unsigned short* orow = op + (size_t)qrow * D;
@@ -331,23 +357,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
 
 }  // namespace
 
-int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream) {
+template <bool SPLIT>
+static int launch_4w(const FwdArgs& a, int D, hipStream_t stream) {
   const int n_qb = (a.Nq + 127) / 128;
-  const long long grid = (long long)n_qb * a.B * a.H;
+  const long long grid = (long long)n_qb * a.B * a.H * (SPLIT ? a.n_splits : 1);
   if (grid > 0x7fffffffLL) return -8;
   const dim3 g((unsigned)grid), blk(256);
   if (D == 128) {
     if (a.pre_scale)
-      attn_fwd_bf16_4w_kernel<128, true><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<128, true, SPLIT><<<g, blk, 0, stream>>>(a);
     else
-      attn_fwd_bf16_4w_kernel<128, false><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<128, false, SPLIT><<<g, blk, 0, stream>>>(a);
   } else {
     if (a.pre_scale)
-      attn_fwd_bf16_4w_kernel<64, true><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<64, true, SPLIT><<<g, blk, 0, stream>>>(a);
     else
-      attn_fwd_bf16_4w_kernel<64, false><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<64, false, SPLIT><<<g, blk, 0, stream>>>(a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream) {
+  return launch_4w<false>(a, D, stream);
+}
+
+int launch_attn_fwd_bf16_4w_split(const FwdArgs& a, int D, hipStream_t stream) {
+  return launch_4w<true>(a, D, stream);
 }
 
 }  // namespace attn89

@@ -36,6 +36,13 @@ struct FwdArgs {
   float c_pre;
   int pre_scale;  // 1 when c_pre must be applied
   int causal;
+  // Split keys (attn_fwd_splitkv only): workgroup split s covers key tiles
+  // [s * kv_chunk, (s + 1) * kv_chunk) / 64 and writes its normalised partial output
+  // (fp32, [n_splits][B][H][Nq][D]) and partial LSE ([n_splits][B][H][Nq]).
+  int n_splits;
+  int kv_chunk;   // keys per split, a multiple of 64
+  float* o_part;
+  float* lse_part;
 };
 
 __device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int nk) {

@@ -13,6 +13,15 @@ namespace attn89 {
 // and 4-wave workgroups of 128 rows (any supported D).
 int launch_attn_fwd_bf16_pp(const FwdArgs& a, int D, hipStream_t stream);
 int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream);
+// 4-wave kernel over one key range per workgroup (FwdArgs n_splits, kv_chunk,
+// o_part, lse_part), partial results only
+int launch_attn_fwd_bf16_4w_split(const FwdArgs& a, int D, hipStream_t stream);
+
+// Split keys: number of splits actually used for a request (<= 0: automatic, aiming
+// at two workgroups per CU) and the keys per split (*chunk, a multiple of 64).
+int splitkv_plan(int B, int H, int Nq, int Nk, int requested, int num_cus, int* chunk);
+// The split kernel, then the merge into o and lse.
+int launch_attn_splitkv(const FwdArgs& a, int D, hipStream_t stream);
 int launch_attn_fwd_f32(const FwdArgs& a, int D, hipStream_t stream);
 
 // Workspace layout of the materialised baseline: S (fp32) then P (bf16), both

@@ -83,9 +83,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                         half a key tile apart (one on the matrix cores while
  *                         the other computes its softmax); one workgroup per CU
  *   ATTN_KERNEL_FOURWAVE  4-wave workgroups of 128 query rows, two per CU
- *   ATTN_KERNEL_AUTO      (default) ping-pong when D = 128 and its grid,
- *                         ceil(Nq/256)*B*H workgroups, covers every compute
- *                         unit; otherwise four-wave
+ *   ATTN_KERNEL_AUTO      (default) ping-pong when D = 128, Nq >= 256 and its
+ *                         grid, ceil(Nq/256)*B*H workgroups, covers every
+ *                         compute unit; otherwise four-wave
  *
  * The setting is process-wide and not synchronised: change it only while no
  * other thread calls attn_fwd.  Returns the previous setting, or
@@ -162,6 +162,34 @@ int attn_partial(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int Nq, int Nk, int D, float scale, int causal,
                  const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * attn_fwd_splitkv -- the fused forward (same arguments, semantics and
+ * tolerance as attn_fwd, bfloat16) with the keys of every (batch, head, query
+ * block) split into ranges that run as separate workgroups, for calls with few
+ * queries and many keys (decoding against a KV cache: Nq small, Nk large or
+ * kv_lens ragged), where one workgroup per (batch, head) would leave the GPU
+ * idle.  Each range writes its normalised partial output O_s (fp32) and
+ * LSE_s to the workspace; a merge launch combines them:
+ * LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the online
+ * correction of page "Attention softmax fusion", section "The tile loop",
+ * applied to whole key ranges).  Two launches; the split kernel is the 4-wave
+ * bf16 kernel restricted to a key range.
+ *
+ * num_splits: requested number of key ranges (<= 0: automatic, about two
+ * workgroups per compute unit); it is clamped to [1, min(256, ceil(Nk / 64))] and the
+ * ranges are whole 64-key tiles, so fewer ranges may be used
+ * (attn_splitkv_num_splits returns the number).  `workspace`: caller-owned
+ * device buffer of at least attn_splitkv_workspace_bytes(B, H, Nq, Nk, D,
+ * num_splits) bytes (the same num_splits), 256-byte aligned
+ * (ATTN_ERR_WORKSPACE otherwise); its contents on return are unspecified.
+ */
+int attn_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_splits);
+size_t attn_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int D, int num_splits);
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                     const int32_t* kv_lens, int num_splits, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* attn_strerror -- a static, NUL-terminated description of a status code. */
 const char* attn_strerror(int status);

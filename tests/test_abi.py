@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
                             "attn_abi_version", "attn_fwd_select_kernel",
                             "softmax_rows_f32", "softmax_rows_unfused_workspace_bytes",
                             "softmax_rows_unfused_f32", "attn_partial",
-                            "attn_partial_workspace_bytes"])
+                            "attn_partial_workspace_bytes", "attn_fwd_splitkv",
+                            "attn_splitkv_num_splits", "attn_splitkv_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -140,3 +141,22 @@ def test_softmax_rows_rejects_bad_arguments(lib):
     assert lib.softmax_rows_unfused_f32(p, p, 1000, 8, None, need, None) == -6
     assert lib.softmax_rows_unfused_f32(p, p, 1000, 8, ctypes.c_void_p(0x10040), need,
                                         None) == -6
+
+
+def test_splitkv_plan_and_checks(lib):
+    """The number of key ranges used for an explicit request (whole 64-key tiles) and
+    the host-side checks of attn_fwd_splitkv (nothing is launched)."""
+    assert lib.attn_splitkv_num_splits(1, 1, 1, 100, 5) == 2        # 2 tiles
+    assert lib.attn_splitkv_num_splits(1, 1, 1, 640, 1) == 1
+    assert lib.attn_splitkv_num_splits(1, 1, 1, 640, 3) == 3        # 4 + 4 + 2 tiles
+    assert lib.attn_splitkv_num_splits(1, 1, 1, 640, 4) == 4        # 3 + 3 + 3 + 1
+    assert lib.attn_splitkv_num_splits(1, 1, 1, 640, 6) == 5        # 2 tiles each
+    assert lib.attn_splitkv_num_splits(0, 1, 1, 640, 6) == -2
+    assert lib.attn_splitkv_workspace_bytes(1, 1, 1, 640, 96, 3) == 0   # unsupported D
+    need = lib.attn_splitkv_workspace_bytes(2, 3, 5, 640, 128, 3)
+    assert need >= 3 * 2 * 3 * 5 * (128 + 1) * 4 and need % 256 == 0
+    p = ctypes.c_void_p(0x10000)
+    args = [p, p, p, p, p, 2, 3, 5, 640, 128, ctypes.c_float(0.1), 0, None, 3]
+    assert lib.attn_fwd_splitkv(*args, p, need - 1, None) == -6
+    assert lib.attn_fwd_splitkv(*args, None, need, None) == -6
+    assert lib.attn_fwd_splitkv(None, *args[1:], p, need, None) == -1
