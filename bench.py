@@ -109,6 +109,22 @@ def softmax_traffic():
     return None
 
 
+def decode_traffic():
+    """Split-key decode HBM bytes per call (both launches) from the committed profile."""
+    path = os.path.join(ROOT, "profiles", "traffic_decode_b1h8_nq1_d128_nk_sweep.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    from exact_attention_89_amd.traffic import _decode_hash
+    if rec.get("kernel_source_hash") != _decode_hash():
+        return None
+    for e in rec.get("entries", []):
+        if all(e[k] == DECODE[k] for k in ("B", "H", "Nq", "Nk", "D")):
+            return e["read_bytes"] + e["write_bytes"]
+    return None
+
+
 def softmax_cpu_baseline(x, budget_s):
     """Time the fp64 row-softmax oracle on whole rows of the input until budget_s."""
     from threadpoolctl import threadpool_info
@@ -260,7 +276,8 @@ def bench_decode(args):
                    "num_splits": int(api.load_library().attn_splitkv_num_splits(B, H, Nq, Nk, 0)),
                    "fused_attn_fwd_ms_per_step": round(fused_ms, 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": decode_traffic()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

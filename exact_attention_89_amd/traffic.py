@@ -25,7 +25,9 @@ The claims being measured:
   hide the difference, so lengths are swept;
 * row softmax (page "Kernel Fusion and the Memory Wall", section "Softmax needs a
   global row statistic"): four reads and two writes per row unfused, one read and
-  one write fused while the row fits on chip.
+  one write fused while the row fits on chip;
+* split-key decode: K and V are read once whatever the number of key ranges; the
+  partial results the ranges hand to the merge are small beside them.
 """
 
 from __future__ import annotations
@@ -55,6 +57,12 @@ def _kernel_hash():
     """Sources of the bf16 fused attention kernels."""
     return _hash(("attn_fwd_bf16_pp.hip", "attn_fwd_bf16_4w.hip", "attn_bf16_tiles.hpp",
                   "common.hpp"))
+
+
+def _decode_hash():
+    """Sources of the split-key decode path (the 4-wave kernel plus the merge)."""
+    return _hash(("attn_fwd_bf16_4w.hip", "attn_bf16_tiles.hpp", "common.hpp",
+                  "attn_splitkv.hip"))
 
 
 def _softmax_hash():
@@ -104,6 +112,31 @@ def cmd_run(a):
             del x, y
             torch.cuda.empty_cache()
         manifest["kernel_source_hash"] = _softmax_hash()
+    elif a.impl == "decode":
+        for Nk in a.Nk:
+            q = torch.randn((a.B, a.H, a.Nq, a.D), device=dev, dtype=torch.bfloat16)
+            k = torch.randn((a.B, a.H, Nk, a.D), device=dev, dtype=torch.bfloat16)
+            v = torch.randn_like(k)
+            o = torch.empty_like(q)
+            lse = torch.empty((a.B, a.H, a.Nq), device=dev, dtype=torch.float32)
+            ws = torch.empty(api.attn_splitkv_workspace_bytes(a.B, a.H, a.Nq, Nk, a.D, 0),
+                             dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+            print(f"[traffic] decode Nk={Nk}", flush=True)
+            for _ in range(a.calls):
+                api.attn_fwd_splitkv(q, k, v, workspace=ws, out=o, lse=lse)
+            torch.cuda.synchronize()
+            manifest["entries"].append({
+                "Nk": Nk, "B": a.B, "H": a.H, "Nq": a.Nq, "D": a.D,
+                "num_splits": int(api.load_library().attn_splitkv_num_splits(
+                    a.B, a.H, a.Nq, Nk, 0)),
+                "dispatches_per_call": 2,
+                "algorithmic_bytes": (2 * a.B * a.H * Nk * a.D * 2
+                                      + 2 * a.B * a.H * a.Nq * a.D * 2 + 4 * a.B * a.H * a.Nq),
+            })
+            del q, k, v, o, lse, ws
+            torch.cuda.empty_cache()
+        manifest["kernel_source_hash"] = _decode_hash()
     else:
         for N in a.N:
             for causal in a.causal:
@@ -286,18 +319,52 @@ def cmd_summarize_softmax(a):
     print("\n".join(lines))
 
 
+def cmd_summarize_decode(a):
+    """Split-key decode: bytes per call against K + V read once."""
+    man, cal, entries = _load_run(a.dir, "decode")
+    rec = {"calibration": cal, "kernel_source_hash": man.get("kernel_source_hash"),
+           "commands": a.command or [], "entries": entries}
+    mib = float(1 << 20)
+    lines = ["# Device-memory traffic: split-key decode (one query per head)", ""]
+    lines += [f"    {c}" for c in a.command or []]
+    lines += ["", f"* calibration (1 GiB copy in the same process): FETCH_SIZE x "
+              f"{cal['fetch_factor']:.3f}, WRITE_SIZE x {cal['write_factor']:.3f} = true bytes",
+              "", "Calibrated MiB per call (both launches: the split kernel and the merge).", "",
+              "| B | H | Nq | Nk | D | splits | algorithmic | read | write | split kernel read "
+              "| split kernel write | merge read | merge write | (read + write) / algorithmic |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for e in entries:
+        pk = e["per_kernel"]
+        sk = next((v for n, v in pk.items() if "4w" in n), [float("nan")] * 2)
+        mk = next((v for n, v in pk.items() if "merge" in n), [float("nan")] * 2)
+        lines.append(f"| {e['B']} | {e['H']} | {e['Nq']} | {e['Nk']} | {e['D']} | "
+                     f"{e['num_splits']} | {e['algorithmic_bytes'] / mib:.2f} | "
+                     f"{e['read_bytes'] / mib:.2f} | {e['write_bytes'] / mib:.2f} | "
+                     f"{sk[0] / mib:.2f} | {sk[1] / mib:.2f} | {mk[0] / mib:.2f} | "
+                     f"{mk[1] / mib:.2f} | "
+                     f"{(e['read_bytes'] + e['write_bytes']) / e['algorithmic_bytes']:.3f} |")
+    with open(a.out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(a.out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--impl", choices=["fused", "partial", "materialized", "softmax_fused",
-                                      "softmax_unfused"], required=True)
+                                      "softmax_unfused", "decode"], required=True)
     r.add_argument("--label", default=None, help="manifest label (e.g. headline)")
     r.add_argument("--N", type=int, nargs="+", default=[1024, 2048, 4096, 8192, 16384, 32768])
     r.add_argument("--causal", type=int, nargs="+", default=[1, 0])
     r.add_argument("--B", type=int, default=1)
     r.add_argument("--H", type=int, default=8)
     r.add_argument("--D", type=int, default=128)
+    r.add_argument("--Nq", type=int, default=1, help="queries per head of the decode sweep")
+    r.add_argument("--Nk", type=int, nargs="+", default=[8192, 16384, 32768, 65536, 131072],
+                   help="cache lengths of the decode sweep")
     r.add_argument("--calls", type=int, default=2)
     r.add_argument("--copy-mib", type=int, default=1024)
     r.add_argument("--cols", type=int, nargs="+", default=[1024, 4096, 8192, 16384, 65536],
@@ -317,11 +384,17 @@ def main():
     ss.add_argument("--out-json", required=True)
     ss.add_argument("--out-md", required=True)
     ss.add_argument("--command", action="append")
+    sd = sub.add_parser("summarize-decode")
+    sd.add_argument("--dir", required=True)
+    sd.add_argument("--out-json", required=True)
+    sd.add_argument("--out-md", required=True)
+    sd.add_argument("--command", action="append")
     a = ap.parse_args()
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     {"run": cmd_run, "summarize": cmd_summarize,
-     "summarize-softmax": cmd_summarize_softmax}[a.cmd](a)
+     "summarize-softmax": cmd_summarize_softmax,
+     "summarize-decode": cmd_summarize_decode}[a.cmd](a)
 
 
 if __name__ == "__main__":
