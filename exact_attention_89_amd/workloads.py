@@ -16,6 +16,10 @@ Recipe (numpy ``default_rng(seed)``; draw order as listed):
   Q, K0, V, and forms K = K0 + 0.002 * j * u in float32 (j the 0-based key
   index, one u for all heads) before rounding to bf16.  Later keys then keep
   raising the running maximum for queries with q.u > 0.
+* FP8 inputs: Q, K, V drawn as above (float32), then each tensor is quantised to
+  OCP E4M3 codes with one factor per tensor: descale = fp32(amax / 448), codes =
+  E4M3(x / descale) rounded to nearest even (torch's float8_e4m3fn cast, after
+  clipping to +-448).  Both sides consume the codes and the descales.
 """
 
 from __future__ import annotations
@@ -34,6 +38,34 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     lsb = (u >> 16) & 1
     u = (u + 0x7FFF + lsb) & 0xFFFF0000
     return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+
+
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3(x: np.ndarray):
+    """(codes uint8, descale float) of a float32 tensor, one descale for the tensor."""
+    import torch
+
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    descale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    y = np.clip(x / np.float32(descale), -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.ascontiguousarray(codes), descale
+
+
+def random_fp8_case(seed: int, B: int, H: int, Nq: int, Nk: int, D: int, std: float = 1.0):
+    """A seeded FP8 case: N(0, std^2) Q and K, N(0, 1) V, each quantised to E4M3.
+
+    Returns (q8, k8, v8, (q_descale, k_descale, v_descale)).
+    """
+    rng = np.random.default_rng(seed)
+    q = (std * rng.standard_normal((B, H, Nq, D), dtype=np.float32)).astype(np.float32)
+    k = (std * rng.standard_normal((B, H, Nk, D), dtype=np.float32)).astype(np.float32)
+    v = rng.standard_normal((B, H, Nk, D), dtype=np.float32)
+    (q8, qd), (k8, kd), (v8, vd) = (quantize_e4m3(t) for t in (q, k, v))
+    return q8, k8, v8, (qd, kd, vd)
 
 
 @dataclasses.dataclass

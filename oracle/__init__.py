@@ -8,4 +8,10 @@ from .attn_oracle import (  # noqa: F401
     kv_length,
     valid_keys,
 )
+from .fp8_oracle import (  # noqa: F401
+    attention_fp8_oracle,
+    attention_fp8_oracle_rows,
+    dequantize,
+    e4m3_decode,
+)
 from .softmax_oracle import softmax_rows, softmax_rows_four_pass  # noqa: F401
