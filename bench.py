@@ -283,6 +283,85 @@ def bench_decode(args):
     print(json.dumps(line), flush=True)
 
 
+PEAK_FP8_TFLOPS = 5000.0
+
+
+def bench_fp8(args):
+    """The fused forward on E4M3 inputs at the throughput workload's shape."""
+    import numpy as np
+    import torch
+
+    import exact_attention_89_amd.workloads as W
+    from exact_attention_89_amd import api
+    api.load_library()
+    name = W.HEADLINE
+    w = W.WORKLOADS[name]
+    log(f"[bench] generating {name} as E4M3 codes")
+    q8, k8, v8, ds, lens = W.generate_fp8(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q8, k8, v8))
+    o = torch.empty(qd.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for s_, e in ev:
+            s_.record(stream)
+            fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        launch = [s_.elapsed_time(e) for s_, e in ev]
+        return ev[0][0].elapsed_time(ev[-1][1]) / args.steps, launch
+
+    ms, launch = timed(lambda: api.attn_fwd_fp8(qd, kd, vd, *ds, scale=w.scale, causal=w.causal,
+                                                out=o, lse=lse))
+    assert not torch.isnan(o).any().item(), "NaN in the output"
+    flops = w.metric_flops()
+    value = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (float(np.mean(launch)) * 1e-3) / 1e12
+    log(f"[bench] fp8 {name}: {ms:.4f} ms/step, launch median {np.median(launch):.4f} ms, p10 "
+        f"{np.percentile(launch, 10):.4f}, p90 {np.percentile(launch, 90):.4f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        import oracle
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+        t0, heads = time.perf_counter(), 0
+        for h in range(w.H):
+            oracle.attention_fp8_oracle(q8[:, h:h + 1], k8[:, h:h + 1], v8[:, h:h + 1], w.scale,
+                                        *ds, causal=w.causal)
+            heads += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": flops / w.H * heads / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{heads} of {w.H} heads of the E4M3 workload, every query row, fp64 "
+                         f"numpy oracle of the dequantised inputs, {dt:.1f} s wall; flops "
+                         f"counted as in the metric"}
+    line = {
+        "metric": "fused attn fwd TFLOP/s, E4M3 inputs (B,H,N,D=1,32,8192,128 causal)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "fp8_causal_b1h32_n8192_d128", "B": w.B, "H": w.H, "Nq": w.Nq,
+                   "Nk": w.Nk, "D": w.D, "causal": w.causal, "seed": w.seed,
+                   "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,12 +371,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--op", choices=["attention", "partial", "materialized", "softmax_rows",
-                                     "decode"],
+                                     "decode", "fp8"],
                     default="attention",
                     help="attention: the fused attention forward (default); partial: QK^T + "
                          "softmax fused, P through device memory, then P V; materialized: the "
                          "three-launch baseline; softmax_rows: the standalone row softmax; "
-                         "decode: split-key attention for one query against a long cache")
+                         "decode: split-key attention for one query against a long cache; "
+                         "fp8: the fused forward on E4M3 inputs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the fused "
@@ -305,11 +385,12 @@ def main():
               "would be N independent copies of this one", file=sys.stderr)
         sys.exit(2)
 
-    if args.op in ("softmax_rows", "decode"):
+    if args.op in ("softmax_rows", "decode", "fp8"):
         if not os.path.exists(os.path.join(ROOT, "exact_attention_89_amd", "libattn89.so")):
             from exact_attention_89_amd import build
             build.build()
-        return bench_softmax(args) if args.op == "softmax_rows" else bench_decode(args)
+        return {"softmax_rows": bench_softmax, "decode": bench_decode,
+                "fp8": bench_fp8}[args.op](args)
 
     import numpy as np
     import torch

@@ -38,6 +38,7 @@ EXPORTS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
     "attn_fwd_select_kernel": (_I, [_I]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _I, _P, _P]),
     "attn_materialized_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "attn_materialized": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ,
                                _P]),
@@ -159,6 +160,34 @@ def attn_fwd_f32(q, k, v, scale: Optional[float] = None, causal: bool = False, k
     """Fused attention forward, fp32 in/out.  Returns (o, lse)."""
     import torch
     return _call_fwd("attn_fwd_f32", q, k, v, scale, causal, kv_lens, out, lse, torch.float32)
+
+
+def attn_fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
+                 scale: Optional[float] = None, causal: bool = False, kv_lens=None, out=None,
+                 lse=None):
+    """Fused attention forward on E4M3 codes (uint8 or float8_e4m3fn tensors) with one
+    descale factor per tensor; bf16 output.  Returns (o, lse)."""
+    import torch
+    codes = []
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+            t = t.view(torch.uint8)
+        codes.append(t)
+    torch, q, k, v, kv_lens, (B, H, Nq, Nk, D) = _prep(*codes, kv_lens, torch.uint8)
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if l.shape != (B, H, Nq) or l.dtype != torch.float32 or not l.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    st = load_library().attn_fwd_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Nq, Nk, D,
+        float(scale), float(q_descale), float(k_descale), float(v_descale), int(bool(causal)),
+        kv_lens.data_ptr() if kv_lens is not None else None, _stream_handle(torch, q.device))
+    _check(st, "attn_fwd_fp8")
+    return o, l
 
 
 def attn_materialized_workspace_bytes(B: int, H: int, Nq: int, Nk: int) -> int:

@@ -110,6 +110,21 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return attn89::launch_attn_fwd_bf16_4w(a, D, (hipStream_t)stream);
 }
 
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int H, int Nq, int Nk, int D, float scale, float q_descale, float k_descale,
+                 float v_descale, int causal, const int32_t* kv_lens, void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, kv_lens, 1);
+  if (st != ATTN_OK) return st;
+  for (float d : {q_descale, k_descale, v_descale})
+    if (!(isfinite(d) && d > 0.f)) return ATTN_ERR_SCALE;
+  const float s_eff = scale * q_descale * k_descale;   // the score scale, in fp32
+  if (!isfinite(s_eff)) return ATTN_ERR_SCALE;
+  if (((size_t)Nq + 256) * D >= ((size_t)1 << 31) || ((size_t)Nk + 256) * D >= ((size_t)1 << 31))
+    return ATTN_ERR_TOO_LARGE;
+  attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, s_eff, causal, kv_lens);
+  return attn89::launch_attn_fwd_fp8(a, D, v_descale, (hipStream_t)stream);
+}
+
 int attn_fwd_select_kernel(int which) {
   if (which != ATTN_KERNEL_AUTO && which != ATTN_KERNEL_PINGPONG &&
       which != ATTN_KERNEL_FOURWAVE)

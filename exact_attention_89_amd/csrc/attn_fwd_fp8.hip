@@ -1,0 +1,381 @@
+// attn_fwd_fp8.hip -- the fused attention forward for gfx950 on FP8 inputs: Q, K, V
+// as OCP E4M3 codes with one dequantisation factor per tensor, both products on the
+// FP8 matrix cores (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation), bf16 O, fp32 LSE.
+//
+// The page "Fused Multi-Head Attention" (quantization item of the section on how
+// fused attention combines with other techniques) names FP8 data for the matrix
+// products of a fused kernel.  Everything else is the fused forward of
+// attn_fwd_bf16_4w.hip: scores, mask, online softmax with the exp(m_old - m_new)
+// correction and the P.V product stay in the workgroup (page "Attention softmax
+// fusion", sections "What fused has to mean" and "The tile loop").
+//
+// Arithmetic.  Scores are s = (scale * q_descale * k_descale) * sum_d q8 k8; the
+// products of two E4M3 values are exact in fp32 and are summed in fp32.  The
+// probabilities enter the second product as E4M3: p' = 2^kPShift * exp2(s*c - m),
+// rounded to nearest even by v_cvt_pk_fp8_f32.  The shift keeps p' in E4M3's
+// normal range (relative rounding error <= 2^-4) down to p = 2^-12, and with the
+// exponent reference allowed to lag the row maximum by at most kSlack8 (log2 units)
+// p' <= 2^(kPShift + kSlack8) = 256 < 448, the largest E4M3 value.  The normaliser
+// l sums the unrounded p' in fp32.  O = v_descale * (sum p'_rounded v8) / l, LSE =
+// ln2 * (m + log2 l - kPShift).
+//
+// Layout (one workgroup = 4 waves = 128 query rows of one (batch, head); key tiles
+// of 64).  Scores are computed transposed, S^T = K Q^T: A = 32 keys x 64 dimensions
+// of K (from LDS), B = 64 dimensions x 32 queries of Q^T (in VGPRs for the whole
+// loop).  Lane l feeds row / column l%32 of its operand and 32 consecutive bytes of
+// the reduction dimension (half l/32); the hardware's order inside the reduction
+// does not matter as long as A and B use the same one, which they do.  The score
+// accumulator of 32 keys x 32 queries leaves register r of lane l with key
+// 8*(r/4) + 4*(l/32) + r%4 and query l%32, so the 64 P values of a lane (two 32-key
+// blocks) are exactly the 32 bytes one B operand of O^T = V^T P^T needs: byte
+// 16*kb + r of lane half h is key 32*kb + 8*(r/4) + 4*h + r%4.  The V^T tile in LDS
+// stores each dimension's 64 keys in that order (position 32*h + 16*kb + 4*(r/4) +
+// r%4), so the A operand of a lane is 32 consecutive bytes of one V^T row.
+//
+// Data movement.  K tiles go global -> LDS by buffer_load ... lds (row-major, 16-byte
+// chunks XOR-swizzled by row); V tiles pass through registers, are transposed with
+// byte permutes and written as V^T (chunks swizzled by row).  Both double buffered;
+// the key loop is unrolled by two so every LDS offset is an immediate.
+#include <type_traits>
+
+#include "attn_bf16_tiles.hpp"
+#include "launch.hpp"
+
+namespace attn89 {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kPShift = 6.0f;   // p' = 2^6 * p
+constexpr float kSlack8 = 2.0f;   // lazy-correction slack of the FP8 kernel
+
+template <int D>
+struct Cfg8 {
+  static constexpr int BR = 128;                 // query rows per workgroup
+  static constexpr int BC = 64;                  // keys per tile
+  static constexpr int NT = 256;                 // threads per workgroup
+  static constexpr int ROWB = D;                 // bytes per K row
+  static constexpr int TILE = BC * D;            // bytes per K tile (and per V^T tile)
+  static constexpr int VTROWB = BC;              // bytes per V^T row
+  static constexpr int DMA = TILE / 1024 / 4;    // 1 KiB K loads per wave per tile
+  static constexpr int V_UNITS = (BC / 4) * (D / 8);  // threads staging V (4 keys x 8 dims)
+  static constexpr int DSTEPS = D / 64;          // k-steps of S^T = K Q^T
+  static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
+  static constexpr int LDS = 4 * TILE;           // K double buffer, V^T double buffer
+  static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
+};
+
+// K chunk swizzle (16-byte chunks): the 16 lanes the LDS serves together read one
+// chunk column of 16 consecutive rows; with 128-byte rows two rows span the banks,
+// with 64-byte rows four.  Adding 32 to the row leaves it unchanged.
+template <int D>
+__device__ __forceinline__ int kswz8(int row) {
+  return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+// V^T rows are 64 bytes (4 chunks): four rows span the banks.
+__device__ __forceinline__ int vtswz8(int d) { return (d >> 2) & 3; }
+
+__device__ __forceinline__ i32x8 lds_load32(const lds_u8* base, unsigned off) {
+  const u32x4 lo = lds_load<u32x4>(base, off);
+  const u32x4 hi = lds_load<u32x4>(base, off + 16);
+  return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // formats 0/0: both operands E4M3; no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// the 8-byte load of 8 consecutive dimensions
+__device__ __forceinline__ u32x2 buffer_load8_so(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                                 int soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// PRE: scale <= 0, scores are scaled before they are masked.
+template <int D, bool PRE>
+__global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v_descale) {
+  using C = Cfg8<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+  lds_u8* const lds = (lds_u8*)smem;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int lg = lane >> 5;
+
+  // heaviest query blocks first; consecutive workgroups take different (b, h)
+  const int BH = p.B * p.H;
+  const int n_qb = (p.Nq + C::BR - 1) / C::BR;
+  const int qb = n_qb - 1 - (int)blockIdx.x / BH;
+  const int bh = (int)blockIdx.x % BH;
+  const int b = bh / p.H;
+
+  const unsigned char* qp = (const unsigned char*)p.q + (size_t)bh * p.Nq * D;
+  const unsigned char* kp = (const unsigned char*)p.k + (size_t)bh * p.Nk * D;
+  const unsigned char* vp = (const unsigned char*)p.v + (size_t)bh * p.Nk * D;
+  unsigned short* op = (unsigned short*)p.o + (size_t)bh * p.Nq * D;
+  float* lsep = p.lse + (size_t)bh * p.Nq;
+
+  const int L = clamp_len(p.kv_lens, b, p.Nk);
+  const int q0 = qb * C::BR;
+  const int q_hi = min(q0 + C::BR, p.Nq);
+  const int kv_end = p.causal ? min(L, q_hi) : L;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  const int qw = q0 + wave * 32;
+  const int qrow = qw + lq;
+
+  // ---- Q fragments: dimensions 64s + 32*lg .. + 32 of query qrow (zeros past Nq) ----
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)p.Nq * D);
+  i32x8 qf[C::DSTEPS];
+#pragma unroll
+  for (int s = 0; s < C::DSTEPS; ++s) {
+    const unsigned off = (unsigned)qrow * D + 64 * s + 32 * lg;
+    const u32x4 lo = buffer_load16(qrs, off);
+    const u32x4 hi = buffer_load16(qrs, off + 16);
+    qf[s] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+
+  // ---- K: global -> LDS without registers (swizzled row-major) ----
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)L * D);
+  unsigned koff[C::DMA];
+#pragma unroll
+  for (int n = 0; n < C::DMA; ++n) {
+    const int byte = (wave * C::DMA + n) * 1024 + 16 * lane;
+    const int row = byte / C::ROWB;
+    const int ch = ((byte % C::ROWB) / 16) ^ kswz8<D>(row);
+    koff[n] = (unsigned)row * D + 16 * ch;
+  }
+  auto load_k = [&](int t, int stage) {
+#pragma unroll
+    for (int n = 0; n < C::DMA; ++n)
+      buffer_load16_to_lds(krs, (lds_void*)(lds + stage * C::TILE + (wave * C::DMA + n) * 1024),
+                           koff[n], t * C::BC * D);
+  };
+
+  // ---- V: global -> registers -> LDS as V^T in the P byte order ----
+  // Thread (kg, dg) holds keys 4kg .. 4kg+3 x dimensions 8dg .. 8dg+7 and writes 8
+  // dwords, one per dimension, each the 4 keys' bytes.  Keys 4kg .. 4kg+3 sit at
+  // positions 4*(8h + 4kb + g) .. + 3 of a V^T row, with kb = kg/8, g = (kg%8)/2,
+  // h = kg%2: dword g of logical chunk 2h + kb.
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (unsigned)L * D);
+  const bool v_owner = C::V_UNITS >= C::NT || tid < C::V_UNITS;
+  const int vkg = tid % (C::BC / 4), vdg = tid / (C::BC / 4);
+  const unsigned vgoff = (unsigned)(4 * vkg) * D + 8 * vdg;
+  unsigned vwoff[2];  // V^T byte offset of dimension 8dg + 4i (dimension 8dg + 4i + x: + x rows)
+  const int vchunk = 2 * (vkg & 1) + (vkg >> 3);
+  const int vdw = (vkg >> 1) & 3;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int d = 8 * vdg + 4 * i;
+    // vtswz8(d + x) = vtswz8(d) for x < 4 (d is a multiple of 4)
+    vwoff[i] = d * C::VTROWB + ((vchunk ^ vtswz8(d)) * 16) + 4 * vdw;
+  }
+  u32x2 vreg[4];
+  auto load_v = [&](int t) {
+    if (v_owner) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vreg[r] = buffer_load8_so(vrs, vgoff + r * D, t * C::BC * D);
+    }
+  };
+  auto store_v = [&](int buf) {
+    if (v_owner) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // 4 x 4 byte transpose: keys 0..3 (vreg[k][i]) x dimensions 4i .. 4i+3
+        const unsigned w0 = vreg[0][i], w1 = vreg[1][i], w2 = vreg[2][i], w3 = vreg[3][i];
+        const unsigned lo01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+        const unsigned hi01 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+        const unsigned lo23 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+        const unsigned hi23 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+        const unsigned d4[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                                __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                                __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                                __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          *(__attribute__((address_space(3))) unsigned*)(
+              lds + C::VT0 + buf * C::TILE + vwoff[i] + x * C::VTROWB) = d4[x];
+      }
+    }
+  };
+
+  // ---- fragment read offsets ----
+  // K: row lq of each 32-key block, logical chunks 4s + 2lg and 4s + 2lg + 1
+  unsigned kro[C::DSTEPS][2];
+#pragma unroll
+  for (int s = 0; s < C::DSTEPS; ++s)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      kro[s][c] = lq * C::ROWB + (((4 * s + 2 * lg + c) ^ kswz8<D>(lq)) * 16);
+  // V^T: row lq of each 32-dimension block, logical chunks 2lg and 2lg + 1
+  unsigned vro[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) vro[c] = lq * C::VTROWB + (((2 * lg + c) ^ vtswz8(lq)) * 16);
+
+  auto qk = [&](int stage, f32x16* sacc) {
+#pragma unroll
+    for (int s = 0; s < C::DSTEPS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const lds_u8* base = lds + stage * C::TILE + kb * 32 * C::ROWB;
+        const u32x4 lo = lds_load<u32x4>(base, kro[s][0]);
+        const u32x4 hi = lds_load<u32x4>(base, kro[s][1]);
+        const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        sacc[kb] = mfma_fp8(a, qf[s], s == 0 ? (f32x16){} : sacc[kb]);
+      }
+  };
+
+  auto needs_mask = [&](int t) {
+    const int j0 = t * C::BC;
+    return PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw);
+  };
+  auto apply_mask = [&](int t, f32x16* sacc) {
+    const int j0 = t * C::BC;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        const bool ok = (key < L) & (!p.causal | (key <= qrow));
+        const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
+        sacc[kb][r] = ok ? x : kNegInf;
+      }
+  };
+
+  f32x16 oacc[C::DBLK];
+#pragma unroll
+  for (int d = 0; d < C::DBLK; ++d) oacc[d] = (f32x16){};
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  const float c_exp = p.c_exp;
+
+  auto iteration = [&](const int t, auto par_tag, auto last_tag) {
+    constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool LAST = decltype(last_tag)::value;
+    if (!LAST) {
+      load_k(t + 1, PAR ^ 1);
+      load_v(t + 1);
+    }
+    f32x16 scur[2];
+    qk(PAR, scur);
+    if (needs_mask(t)) apply_mask(t, scur);
+    // row maximum and exponent reference (guard: a row without a valid key so far
+    // keeps m = -inf and uses 0 as its reference)
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
+    mx = max_with_partner(mx) * c_exp;
+    const bool move = mx > m_run + kSlack8;
+    const float m_new = move ? mx : m_run;
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    if (__any(move)) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+    }
+    m_run = m_new;
+    // p' = exp2(s*c - m + kPShift), packed to E4M3: byte 16kb + r <- register r of block kb
+    const float m_sh = m_use - kPShift;
+    i32x8 pf;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float e[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          e[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][4 * w + x], c_exp, -m_sh));
+        lsum += (e[0] + e[1]) + (e[2] + e[3]);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
+        pf[4 * kb + w] = word;
+      }
+    l_run += lsum;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int d = 0; d < C::DBLK; ++d) {
+      const lds_u8* base = lds + C::VT0 + PAR * C::TILE + d * 32 * C::VTROWB;
+      const u32x4 lo = lds_load<u32x4>(base, vro[0]);
+      const u32x4 hi = lds_load<u32x4>(base, vro[1]);
+      const i32x8 va = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      oacc[d] = mfma_fp8(va, pf, oacc[d]);
+    }
+    if (!LAST) {
+      store_v(PAR ^ 1);
+      __syncthreads();
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_v(0);
+    load_k(0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
+  if (n_tiles > 0) store_v(0);
+  __syncthreads();
+  int t = 0;
+  for (; t + 2 < n_tiles; t += 2) {
+    iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
+    iteration(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  if (t + 1 < n_tiles) {
+    iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
+    iteration(t + 1, std::integral_constant<int, 1>{}, std::true_type{});
+  } else if (t < n_tiles) {
+    iteration(t, std::integral_constant<int, 0>{}, std::true_type{});
+  }
+
+  // ---- epilogue: O = v_descale * a / l (0 without a valid key), LSE ----
+  const float l_tot = sum_with_partner(l_run);
+  if (qrow < p.Nq) {
+    const float inv = l_tot > 0.f ? v_descale / l_tot : 0.f;
+    unsigned short* orow = op + (size_t)qrow * D;
+#pragma unroll
+    for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 w = {pack_bf16x2(oacc[d][4 * a + 0] * inv, oacc[d][4 * a + 1] * inv),
+                   pack_bf16x2(oacc[d][4 * a + 2] * inv, oacc[d][4 * a + 3] * inv)};
+        *(u32x2*)(orow + d * 32 + 8 * a + 4 * lg) = w;
+      }
+    if (lg == 0)
+      lsep[qrow] = l_tot > 0.f
+                       ? (m_run + __builtin_amdgcn_logf(l_tot) - kPShift) * kLn2
+                       : kNegInf;
+  }
+}
+
+}  // namespace
+
+int launch_attn_fwd_fp8(const FwdArgs& a, int D, float v_descale, hipStream_t stream) {
+  const int n_qb = (a.Nq + 127) / 128;
+  const long long grid = (long long)n_qb * a.B * a.H;
+  if (grid > 0x7fffffffLL) return -8;
+  const dim3 g((unsigned)grid), blk(256);
+  if (D == 128) {
+    if (a.pre_scale)
+      attn_fwd_fp8_kernel<128, true><<<g, blk, 0, stream>>>(a, v_descale);
+    else
+      attn_fwd_fp8_kernel<128, false><<<g, blk, 0, stream>>>(a, v_descale);
+  } else {
+    if (a.pre_scale)
+      attn_fwd_fp8_kernel<64, true><<<g, blk, 0, stream>>>(a, v_descale);
+    else
+      attn_fwd_fp8_kernel<64, false><<<g, blk, 0, stream>>>(a, v_descale);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+}  // namespace attn89

@@ -23,6 +23,9 @@ int splitkv_plan(int B, int H, int Nq, int Nk, int requested, int num_cus, int* 
 // The split kernel, then the merge into o and lse.
 int launch_attn_splitkv(const FwdArgs& a, int D, hipStream_t stream);
 int launch_attn_fwd_f32(const FwdArgs& a, int D, hipStream_t stream);
+// FP8 (E4M3) forward, 4-wave workgroups; c_exp / c_pre carry scale * q_descale *
+// k_descale, v_descale multiplies the output.
+int launch_attn_fwd_fp8(const FwdArgs& a, int D, float v_descale, hipStream_t stream);
 
 // Workspace layout of the materialised baseline: S (fp32) then P (bf16), both
 // [B][H][Nq][ld] with ld = Nk rounded up to a multiple of 64.

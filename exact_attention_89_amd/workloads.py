@@ -149,3 +149,26 @@ def random_case(seed: int, B: int, H: int, Nq: int, Nk: int, D: int, dtype: str 
     if kv_lens is not None:
         kv_lens = np.asarray(kv_lens, dtype=np.int32)
     return q, k, v, kv_lens
+
+
+def generate_fp8(w: Workload, heads: Optional[int] = None):
+    """The draws of ``generate`` quantised per tensor to E4M3 instead of rounded to bf16.
+
+    Returns (q8, k8, v8, (q_descale, k_descale, v_descale), kv_lens).
+    """
+    rng = np.random.default_rng(w.seed)
+    if w.drift:
+        rng.standard_normal(w.D, dtype=np.float32)   # keep the draw order of generate
+    q = rng.standard_normal((w.B, w.H, w.Nq, w.D), dtype=np.float32)
+    k = rng.standard_normal((w.B, w.H, w.Nk, w.D), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.H, w.Nk, w.D), dtype=np.float32)
+    kv_lens = None
+    if w.padded:
+        kv_lens = rng.integers(1, w.Nk + 1, size=w.B).astype(np.int32)
+        kv_lens[0] = 0
+    if w.drift:
+        raise ValueError("the drifting-key workload has no FP8 variant")
+    if heads is not None:
+        q, k, v = q[:, :heads], k[:, :heads], v[:, :heads]
+    (q8, qd), (k8, kd), (v8, vd) = (quantize_e4m3(t) for t in (q, k, v))
+    return q8, k8, v8, (qd, kd, vd), kv_lens

@@ -97,6 +97,31 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_select_kernel(int which);
 
 /*
+ * attn_fwd_fp8 -- the fused forward on FP8 inputs (page "Fused Multi-Head
+ * Attention", quantization item of the section on how fused attention combines
+ * with other inference techniques: FP8 data for the matrix products).
+ *
+ * q [B][H][Nq][D], k and v [B][H][Nk][D]: OCP E4M3 codes (one byte each: sign,
+ * 4-bit exponent with bias 7, 3-bit fraction; 0x7F and 0xFF are NaN and must not
+ * occur).  The values they stand for are q_descale * q, k_descale * k and
+ * v_descale * v (one float32 factor per tensor, positive and finite, else
+ * ATTN_ERR_SCALE).  o [B][H][Nq][D]: bfloat16 (round-to-nearest-even); lse
+ * [B][H][Nq]: float32.  Same masks, conventions (fully masked rows: O = 0,
+ * LSE = -inf) and errors as attn_fwd; a single kernel launch.
+ *
+ * Arithmetic: Q.K^T and P.V run on FP8 matrix instructions with fp32
+ * accumulation; scores are scaled by fp32(scale * q_descale * k_descale); the
+ * softmax statistics stay in fp32; the probabilities are rounded to E4M3 (after
+ * a factor 2^6 that keeps them in E4M3's normal range) before P.V, so each
+ * weight carries a relative error of at most 2^-4 where p >= 2^-12 times the
+ * row maximum's weight; the normaliser sums the unrounded weights.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Nq, int Nk, int D, float scale, float q_descale,
+                 float k_descale, float v_descale, int causal, const int32_t* kv_lens,
+                 void* stream);
+
+/*
  * attn_fwd_f32 -- the same fused forward for float32 inputs and output.
  * Same arguments and semantics as attn_fwd, with float32 q, k, v, o.  All
  * arithmetic is fp32 (no rounding of P).
