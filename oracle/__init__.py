@@ -14,4 +14,5 @@ from .fp8_oracle import (  # noqa: F401
     dequantize,
     e4m3_decode,
 )
+from .varlen_oracle import attention_varlen_oracle, seq_spans  # noqa: F401
 from .softmax_oracle import softmax_rows, softmax_rows_four_pass  # noqa: F401
