@@ -109,6 +109,18 @@ def softmax_traffic():
     return None
 
 
+def fp8_traffic():
+    """FP8 fused forward HBM bytes per launch at the throughput shape, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic_fp8_causal_b1h32_n8192_d128.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    from exact_attention_89_amd.traffic import _fp8_hash
+    e = rec.get("fp8", {})
+    return e.get("bytes_per_launch") if e.get("kernel_source_hash") == _fp8_hash() else None
+
+
 def decode_traffic():
     """Split-key decode HBM bytes per call (both launches) from the committed profile."""
     path = os.path.join(ROOT, "profiles", "traffic_decode_b1h8_nq1_d128_nk_sweep.json")
@@ -356,7 +368,7 @@ def bench_fp8(args):
                    "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": fp8_traffic()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

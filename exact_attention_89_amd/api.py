@@ -38,6 +38,8 @@ EXPORTS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
     "attn_fwd_select_kernel": (_I, [_I]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                             _P]),
     "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _I, _P, _P]),
     "attn_materialized_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "attn_materialized": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ,
@@ -160,6 +162,58 @@ def attn_fwd_f32(q, k, v, scale: Optional[float] = None, causal: bool = False, k
     """Fused attention forward, fp32 in/out.  Returns (o, lse)."""
     import torch
     return _call_fwd("attn_fwd_f32", q, k, v, scale, causal, kv_lens, out, lse, torch.float32)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: Optional[int] = None,
+                    max_seqlen_k: Optional[int] = None, scale: Optional[float] = None,
+                    causal: bool = False, out=None, lse=None):
+    """Fused forward over packed variable-length sequences, bf16.
+
+    q [total_q, H, D], k and v [total_k, H, D] (token-major); cu_seqlens_q / _k: B + 1
+    cumulative offsets (int32, device or host).  Returns (o [total_q, H, D] bf16,
+    lse [H, total_q] fp32).  The longest lengths are taken from the offsets when not
+    given (a host copy of them)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a bf16 GPU tensor")
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [tokens, H, D]")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    if k.shape[1:] != (H, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} "
+                         f"v {tuple(v.shape)}")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    cus = []
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if not isinstance(cu, torch.Tensor):
+            cu = torch.tensor(cu, dtype=torch.int32)
+        cus.append(cu.to(device=q.device, dtype=torch.int32).contiguous())
+    cu_q, cu_k = cus
+    B = cu_q.numel() - 1
+    if B < 1 or cu_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold B + 1 >= 2 offsets each")
+    if max_seqlen_q is None or max_seqlen_k is None:
+        hq, hk = cu_q.cpu(), cu_k.cpu()
+        if max_seqlen_q is None:
+            max_seqlen_q = max(1, int((hq[1:] - hq[:-1]).max()))
+        if max_seqlen_k is None:
+            max_seqlen_k = max(1, int((hk[1:] - hk[:-1]).max()))
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if l.shape != (H, total_q) or l.dtype != torch.float32 or not l.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [H, total_q] tensor")
+    st = load_library().attn_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), cu_q.data_ptr(),
+        cu_k.data_ptr(), B, H, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D,
+        float(scale), int(bool(causal)), _stream_handle(torch, q.device))
+    _check(st, "attn_fwd_varlen")
+    return o, l
 
 
 def attn_fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,

@@ -125,6 +125,32 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
   return attn89::launch_attn_fwd_fp8(a, D, v_descale, (hipStream_t)stream);
 }
 
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int H,
+                    int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
+                    float scale, int causal, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4)) return ATTN_ERR_ALIGN;
+  if (max_seqlen_q < 1 || max_seqlen_k < 1) return ATTN_ERR_SHAPE;
+  // the common checks on the packed tensors: one "batch" of total_q / total_k rows of H*D
+  int st = check_common(q, k, v, o, lse, 1, H, total_q, total_k, D, scale, nullptr, 2);
+  if (st != ATTN_OK) return st;
+  if (B < 1) return ATTN_ERR_SHAPE;
+  // per-sequence byte offsets (rows H*D apart, plus a tile of slack) stay below 2^31
+  const size_t row_bytes = (size_t)H * D * 2;
+  if (((size_t)max_seqlen_q + 256) * row_bytes >= ((size_t)1 << 31) ||
+      ((size_t)max_seqlen_k + 256) * row_bytes >= ((size_t)1 << 31))
+    return ATTN_ERR_TOO_LARGE;
+  if ((long long)((max_seqlen_q + 127) / 128) * B * H > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, max_seqlen_q, max_seqlen_k, scale,
+                                causal, nullptr);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  return attn89::launch_attn_fwd_bf16_4w_varlen(a, D, (hipStream_t)stream);
+}
+
 int attn_fwd_select_kernel(int which) {
   if (which != ATTN_KERNEL_AUTO && which != ATTN_KERNEL_PINGPONG &&
       which != ATTN_KERNEL_FOURWAVE)

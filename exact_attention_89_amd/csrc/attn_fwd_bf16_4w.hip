@@ -69,8 +69,12 @@ struct Cfg {
 // instantiation keeps that branch out of the common kernel).
 // SPLIT: the workgroup covers one key range of the row block and writes a partial
 // result (normalised O_r in fp32 and LSE_r) for the merge of attn_splitkv.hip.
-template <int D, bool PRE, bool SPLIT>
+// VARLEN: packed variable-length sequences (FwdArgs cu_q, cu_k): Q, K, V and O are
+// [tokens][H][D], sequence b owns tokens [cu[b], cu[b+1]), rows are H*D apart; Nq
+// and Nk are the longest sequence lengths the grid and the checks were sized for.
+template <int D, bool PRE, bool SPLIT, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
+  static_assert(!(SPLIT && VARLEN), "split keys over packed sequences is not provided");
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
   lds_u8* const lds = (lds_u8*)smem;
@@ -93,15 +97,35 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   const int bh = wg_id % BH;
   const int b = bh / p.H;
 
-  const unsigned short* qp = (const unsigned short*)p.q + (size_t)bh * p.Nq * D;
-  const unsigned short* kp = (const unsigned short*)p.k + (size_t)bh * p.Nk * D;
-  const unsigned short* vp = (const unsigned short*)p.v + (size_t)bh * p.Nk * D;
-  unsigned short* op = (unsigned short*)p.o + (size_t)bh * p.Nq * D;
-  float* lsep = p.lse + (size_t)bh * p.Nq;
+  // rows of this (batch, head): nq queries and L valid keys, ld elements apart
+  const int ld = VARLEN ? p.H * D : D;
+  size_t qbase, kbase;
+  int nq, L;
+  float* lsep;
+  if (VARLEN) {
+    const int h = bh % p.H;
+    const SeqSpan sq = seq_span(p.cu_q, b, p.total_q, p.Nq);
+    const SeqSpan sk = seq_span(p.cu_k, b, p.total_k, p.Nk);
+    nq = sq.len;
+    L = sk.len;
+    qbase = (size_t)sq.start * ld + (size_t)h * D;
+    kbase = (size_t)sk.start * ld + (size_t)h * D;
+    lsep = p.lse + (size_t)h * p.total_q + sq.start;
+    if (qb * C::BR >= nq) return;   // the whole workgroup: past this sequence's queries
+  } else {
+    nq = p.Nq;
+    L = clamp_len(p.kv_lens, b, p.Nk);              // valid keys of this sequence
+    qbase = (size_t)bh * p.Nq * D;
+    kbase = (size_t)bh * p.Nk * D;
+    lsep = p.lse + (size_t)bh * p.Nq;
+  }
+  const unsigned short* qp = (const unsigned short*)p.q + qbase;
+  const unsigned short* kp = (const unsigned short*)p.k + kbase;
+  const unsigned short* vp = (const unsigned short*)p.v + kbase;
+  unsigned short* op = (unsigned short*)p.o + qbase;
 
-  const int L = clamp_len(p.kv_lens, b, p.Nk);      // valid keys of this sequence
   const int q0 = qb * C::BR;
-  const int q_hi = min(q0 + C::BR, p.Nq);
+  const int q_hi = min(q0 + C::BR, nq);
   const int kv_end = p.causal ? min(L, q_hi) : L;    // keys any row of the block sees
   const int n_tiles_all = (kv_end + C::BC - 1) / C::BC;
   // key tiles [t_begin, n_tiles) of this workgroup (all of them unless split)
@@ -112,40 +136,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop ----
   // Buffer loads: rows past Nq (and below, keys past kv_len) read as zeros.
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)p.Nq * D * 2);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)((nq - 1) * ld + D) * 2);
   bf16x8 qf[C::DSTEPS];
 #pragma unroll
   for (int s = 0; s < C::DSTEPS; ++s)
     qf[s] = __builtin_bit_cast(bf16x8,
-                               buffer_load16(qrs, ((unsigned)qrow * D + 16 * s + 8 * lg) * 2));
+                               buffer_load16(qrs, ((unsigned)qrow * ld + 16 * s + 8 * lg) * 2));
 
   // ---- K: global -> LDS without registers ----
   // Load n of this wave writes tile bytes [m*1024, m*1024 + 1024), m = wave*DMA + n,
   // lane i the 16 bytes at m*1024 + 16*i; the lane fetches the global chunk the
   // swizzle puts there.  The tile start is the scalar offset of the load.
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)L * D * 2);
+  // rows past L read as zeros (the last valid row ends at (L - 1) * ld + D)
+  const unsigned kv_bytes = L > 0 ? (unsigned)((L - 1) * ld + D) * 2 : 0u;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, kv_bytes);
   unsigned koff[C::DMA];
 #pragma unroll
   for (int n = 0; n < C::DMA; ++n) {
     const int byte = (wave * C::DMA + n) * 1024 + 16 * lane;
     const int row = byte / C::ROWB;
     const int ch = ((byte % C::ROWB) / 16) ^ kswz<D>(row);
-    koff[n] = ((unsigned)row * D + 8 * ch) * 2;
+    koff[n] = ((unsigned)row * ld + 8 * ch) * 2;
   }
   auto load_k = [&](int t, int stage) {
 #pragma unroll
     for (int n = 0; n < C::DMA; ++n)
       buffer_load16_to_lds(krs, (lds_void*)(lds + stage * C::TILE + (wave * C::DMA + n) * 1024),
-                           koff[n], t * C::BC * D * 2);
+                           koff[n], t * C::BC * ld * 2);
   };
 
   // ---- V: global -> registers -> LDS, transposed ----
   // Thread (kg, dg) holds keys 4kg..4kg+3 x dimensions 8dg..8dg+7 (four 16-byte
   // loads) and writes them as 8 rows of V^T, 4 keys (8 bytes) each.
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (unsigned)L * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, kv_bytes);
   const bool v_owner = C::V_UNITS >= C::NT || tid < C::V_UNITS;
   const int vkg = tid % (C::BC / 4), vdg = tid / (C::BC / 4);
-  const unsigned vgoff = ((unsigned)(4 * vkg) * D + 8 * vdg) * 2;
+  const unsigned vgoff = ((unsigned)(4 * vkg) * ld + 8 * vdg) * 2;
   unsigned vwoff[4];  // V^T byte offset of row 8dg + 2x (row 8dg + 2x + 1: + VTROWB)
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
@@ -157,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     if (v_owner) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vreg[r] = buffer_load16_so(vrs, vgoff + r * D * 2, t * C::BC * D * 2);
+        vreg[r] = buffer_load16_so(vrs, vgoff + r * ld * 2, t * C::BC * ld * 2);
     }
   };
   auto store_v = [&](int buf) {
@@ -322,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   if (SPLIT) {
     // partial result of this key range, fp32 for the merge (an empty range gives
     // O_r = 0 and LSE_r = -inf, weight 0 in the merge)
-    if (qrow < p.Nq) {
+    if (qrow < nq) {
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
       const size_t row = ((size_t)split * BH + bh) * p.Nq + qrow;
       float* orow = p.o_part + row * D;
@@ -338,9 +364,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     }
     return;
   }
-  if (qrow < p.Nq) {
+  if (qrow < nq) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    unsigned short* orow = op + (size_t)qrow * D;
+    unsigned short* orow = op + (size_t)qrow * ld;
 #pragma unroll
     for (int d = 0; d < C::DBLK; ++d)
 #pragma unroll
@@ -357,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
 
 }  // namespace
 
-template <bool SPLIT>
+template <bool SPLIT, bool VARLEN>
 static int launch_4w(const FwdArgs& a, int D, hipStream_t stream) {
   const int n_qb = (a.Nq + 127) / 128;
   const long long grid = (long long)n_qb * a.B * a.H * (SPLIT ? a.n_splits : 1);
@@ -365,24 +391,28 @@ static int launch_4w(const FwdArgs& a, int D, hipStream_t stream) {
   const dim3 g((unsigned)grid), blk(256);
   if (D == 128) {
     if (a.pre_scale)
-      attn_fwd_bf16_4w_kernel<128, true, SPLIT><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<128, true, SPLIT, VARLEN><<<g, blk, 0, stream>>>(a);
     else
-      attn_fwd_bf16_4w_kernel<128, false, SPLIT><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<128, false, SPLIT, VARLEN><<<g, blk, 0, stream>>>(a);
   } else {
     if (a.pre_scale)
-      attn_fwd_bf16_4w_kernel<64, true, SPLIT><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<64, true, SPLIT, VARLEN><<<g, blk, 0, stream>>>(a);
     else
-      attn_fwd_bf16_4w_kernel<64, false, SPLIT><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<64, false, SPLIT, VARLEN><<<g, blk, 0, stream>>>(a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
 int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream) {
-  return launch_4w<false>(a, D, stream);
+  return launch_4w<false, false>(a, D, stream);
 }
 
 int launch_attn_fwd_bf16_4w_split(const FwdArgs& a, int D, hipStream_t stream) {
-  return launch_4w<true>(a, D, stream);
+  return launch_4w<true, false>(a, D, stream);
+}
+
+int launch_attn_fwd_bf16_4w_varlen(const FwdArgs& a, int D, hipStream_t stream) {
+  return launch_4w<false, true>(a, D, stream);
 }
 
 }  // namespace attn89

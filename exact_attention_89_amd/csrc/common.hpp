@@ -43,12 +43,32 @@ struct FwdArgs {
   int kv_chunk;   // keys per split, a multiple of 64
   float* o_part;
   float* lse_part;
+  // Packed variable-length sequences (attn_fwd_varlen only): sequence b owns tokens
+  // [cu_q[b], cu_q[b+1]) of q / o and [cu_k[b], cu_k[b+1]) of k / v; Nq, Nk hold the
+  // longest lengths.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 __device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int nk) {
   if (kv_lens == nullptr) return nk;
   int n = kv_lens[b];
   return n < 0 ? 0 : (n > nk ? nk : n);
+}
+
+// Tokens [cu[b], cu[b+1]) of a packed batch: both ends clamped into [0, total] (the
+// end not below the start) and the length to at most max_len, so that any offsets
+// the caller passes stay inside the tensors the host checks were made for.
+struct SeqSpan {
+  int start;
+  int len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int b, int total, int max_len) {
+  int s = cu[b], e = cu[b + 1];
+  s = s < 0 ? 0 : (s > total ? total : s);
+  e = e < s ? s : (e > total ? total : e);
+  return {s, min(e - s, max_len)};
 }
 
 // round-to-nearest-even float -> bf16 bits, two at a time: one v_cvt_pk_bf16_f32

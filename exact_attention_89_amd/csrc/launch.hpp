@@ -16,6 +16,9 @@ int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream);
 // 4-wave kernel over one key range per workgroup (FwdArgs n_splits, kv_chunk,
 // o_part, lse_part), partial results only
 int launch_attn_fwd_bf16_4w_split(const FwdArgs& a, int D, hipStream_t stream);
+// 4-wave kernel over packed variable-length sequences (FwdArgs cu_q, cu_k, total_q,
+// total_k; Nq, Nk = the longest lengths)
+int launch_attn_fwd_bf16_4w_varlen(const FwdArgs& a, int D, hipStream_t stream);
 
 // Split keys: number of splits actually used for a request (<= 0: automatic, aiming
 // at two workgroups per CU) and the keys per split (*chunk, a multiple of 64).

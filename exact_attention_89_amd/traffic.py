@@ -65,6 +65,11 @@ def _decode_hash():
                   "attn_splitkv.hip"))
 
 
+def _fp8_hash():
+    """Sources of the FP8 fused forward."""
+    return _hash(("attn_fwd_fp8.hip", "attn_bf16_tiles.hpp", "common.hpp"))
+
+
 def _softmax_hash():
     """Sources of the row-softmax kernels."""
     return _hash(("softmax_rows.hip", "common.hpp"))
@@ -147,6 +152,10 @@ def cmd_run(a):
                 o = torch.empty_like(q)
                 lse = torch.empty((a.B, a.H, N), device=dev, dtype=torch.float32)
                 ws = None
+                if a.impl == "fp8":
+                    q, k, v = (torch.randn(shape, device=dev).clamp_(-448, 448)
+                               .to(torch.float8_e4m3fn) for _ in range(3))
+                    o = torch.empty(shape, device=dev, dtype=torch.bfloat16)
                 if a.impl == "materialized":
                     ws = torch.empty(api.attn_materialized_workspace_bytes(a.B, a.H, N, N),
                                      dtype=torch.uint8, device=dev)
@@ -158,6 +167,9 @@ def cmd_run(a):
                 for _ in range(a.calls):
                     if a.impl == "fused":
                         api.attn_fwd(q, k, v, causal=bool(causal), out=o, lse=lse)
+                    elif a.impl == "fp8":
+                        api.attn_fwd_fp8(q, k, v, 1.0, 1.0, 1.0, causal=bool(causal), out=o,
+                                         lse=lse)
                     elif a.impl == "partial":
                         api.attn_partial(q, k, v, causal=bool(causal), workspace=ws,
                                          out=o, lse=lse)
@@ -165,15 +177,17 @@ def cmd_run(a):
                         api.attn_materialized(q, k, v, causal=bool(causal), workspace=ws,
                                               out=o, lse=lse)
                 torch.cuda.synchronize()
+                esize = 1 if a.impl == "fp8" else 2     # bytes per element of Q, K, V
                 manifest["entries"].append({
                     "N": N, "causal": causal, "B": a.B, "H": a.H, "D": a.D,
-                    "dispatches_per_call": {"fused": 1, "partial": 2}.get(a.impl, 3),
-                    "algorithmic_bytes": a.B * a.H * N * a.D * 2 * 4 + a.B * a.H * N * 4,
+                    "dispatches_per_call": {"fused": 1, "fp8": 1, "partial": 2}.get(a.impl, 3),
+                    "algorithmic_bytes": (a.B * a.H * N * a.D * (3 * esize + 2)
+                                          + a.B * a.H * N * 4),
                     "one_score_matrix_16bit_all_heads": a.B * a.H * N * N * 2,
                 })
                 del q, k, v, o, lse, ws
                 torch.cuda.empty_cache()
-        manifest["kernel_source_hash"] = _kernel_hash()
+        manifest["kernel_source_hash"] = _fp8_hash() if a.impl == "fp8" else _kernel_hash()
     with open(a.manifest, "w") as f:
         json.dump(manifest, f, indent=1)
 
@@ -226,7 +240,7 @@ def _load_run(dirpath, impl):
 def cmd_summarize(a):
     """Fused attention against the materialised baseline, plus the headline record."""
     res = {"commands": a.command or []}
-    for impl in ("fused", "partial", "materialized", "headline"):
+    for impl in ("fused", "partial", "materialized", "headline", "fp8"):
         if os.path.exists(os.path.join(a.dir, impl, "manifest.json")):
             man, cal, entries = _load_run(a.dir, impl)
             res[impl] = {"entries": entries, "calibration": cal,
@@ -242,6 +256,19 @@ def cmd_summarize(a):
         with open(a.headline_json, "w") as f:
             json.dump(rec, f, indent=1)
         print(f"headline: read {e['read_bytes'] / 2**20:.1f} MiB, write "
+              f"{e['write_bytes'] / 2**20:.1f} MiB per launch (algorithmic "
+              f"{e['algorithmic_bytes'] / 2**20:.1f} MiB)")
+    if a.fp8_json and "fp8" in res:
+        e = res["fp8"]["entries"][0]
+        rec = {"workload": "fp8_causal_b1h32_n8192_d128",
+               "fp8": {"bytes_per_launch": e["read_bytes"] + e["write_bytes"],
+                       "read_bytes": e["read_bytes"], "write_bytes": e["write_bytes"],
+                       "algorithmic_bytes": e["algorithmic_bytes"],
+                       "kernel_source_hash": res["fp8"]["kernel_source_hash"]},
+               "calibration": res["fp8"]["calibration"], "commands": a.command or []}
+        with open(a.fp8_json, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"fp8: read {e['read_bytes'] / 2**20:.1f} MiB, write "
               f"{e['write_bytes'] / 2**20:.1f} MiB per launch (algorithmic "
               f"{e['algorithmic_bytes'] / 2**20:.1f} MiB)")
     with open(a.out_json, "w") as f:
@@ -355,7 +382,7 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--impl", choices=["fused", "partial", "materialized", "softmax_fused",
-                                      "softmax_unfused", "decode"], required=True)
+                                      "softmax_unfused", "decode", "fp8"], required=True)
     r.add_argument("--label", default=None, help="manifest label (e.g. headline)")
     r.add_argument("--N", type=int, nargs="+", default=[1024, 2048, 4096, 8192, 16384, 32768])
     r.add_argument("--causal", type=int, nargs="+", default=[1, 0])
@@ -379,6 +406,7 @@ def main():
     s.add_argument("--command", action="append")
     s.add_argument("--headline-json", default=None)
     s.add_argument("--headline-name", default="bf16_causal_b1h32_n8192_d128")
+    s.add_argument("--fp8-json", default=None)
     ss = sub.add_parser("summarize-softmax")
     ss.add_argument("--dir", required=True)
     ss.add_argument("--out-json", required=True)

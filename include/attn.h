@@ -97,6 +97,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_select_kernel(int which);
 
 /*
+ * attn_fwd_varlen -- the fused forward over a packed batch of variable-length
+ * sequences (page "Fused Multi-Head Attention", section on how fused attention
+ * combines with other inference techniques: the ragged tensors of continuous
+ * batching), bfloat16 in / out.
+ *
+ * q, o [total_q][H][D], k, v [total_k][H][D]: bfloat16, token-major, the heads of a
+ * token adjacent (rows of one head are H*D elements apart).  Sequence b (0 <= b < B)
+ * owns query tokens [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key/value tokens
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]); its queries attend to its own keys only.
+ * cu_seqlens_q, cu_seqlens_k: device int32 arrays of B + 1 entries, normally
+ * nondecreasing from 0 to total_q / total_k (not read on the host).  The kernel
+ * clamps every entry into [0, total], an end below its start to the start, and a
+ * length above max_seqlen_q / max_seqlen_k to that maximum; query rows outside the
+ * clamped sequences are not written, and rows two clamped sequences share (only
+ * possible when the offsets decrease) hold the result of either.  lse [H][total_q]: float32, the LSE of query
+ * token t and head h at lse[h * total_q + t].  Causal masking is top-left within
+ * each sequence (its key j is visible to its query i iff j <= i); a sequence with no
+ * keys gives O = 0 and LSE = -inf.  One launch of the four-wave kernel.
+ *
+ * Errors as attn_fwd, plus: ATTN_ERR_NULL for a NULL cu_seqlens array,
+ * ATTN_ERR_SHAPE for total_q, total_k, max_seqlen_q or max_seqlen_k < 1,
+ * ATTN_ERR_TOO_LARGE when (max_seqlen + 256) * H * D * 2 bytes reaches 2^31.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int H,
+                    int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
+                    float scale, int causal, void* stream);
+
+/*
  * attn_fwd_fp8 -- the fused forward on FP8 inputs (page "Fused Multi-Head
  * Attention", quantization item of the section on how fused attention combines
  * with other inference techniques: FP8 data for the matrix products).

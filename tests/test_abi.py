@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
                             "softmax_rows_unfused_f32", "attn_partial",
                             "attn_partial_workspace_bytes", "attn_fwd_splitkv",
                             "attn_splitkv_num_splits", "attn_splitkv_workspace_bytes",
-                            "attn_fwd_fp8"])
+                            "attn_fwd_fp8", "attn_fwd_varlen"])
 
 
 def test_every_declared_symbol_is_exported(lib):
