@@ -374,6 +374,12 @@ def bench_fp8(args):
     print(json.dumps(line), flush=True)
 
 
+def versions(torch):
+    """torch / HIP versions and the device name, recorded with every headline line."""
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "device": torch.cuda.get_device_name(0)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,6 +388,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="calls timed with a 512 MiB buffer written before each (0: skip)")
     ap.add_argument("--op", choices=["attention", "partial", "materialized", "softmax_rows",
                                      "decode", "fp8"],
                     default="attention",
@@ -476,6 +484,29 @@ def main():
         f" ms/step, launch median {np.median(launch_ms):.4f} ms, p10 "
         f"{np.percentile(launch_ms, 10):.4f}, p90 {np.percentile(launch_ms, 90):.4f}")
     assert not torch.isnan(o).any().item(), "NaN in the output"
+    launch_stats = {"median": round(float(np.median(launch_ms)), 5),
+                    "p10": round(float(np.percentile(launch_ms, 10)), 5),
+                    "p90": round(float(np.percentile(launch_ms, 90)), 5)}
+    cold = None
+    if args.op == "attention" and args.cold_steps > 0:
+        # cold variant: a 512 MiB buffer is written between calls, so K and V are not
+        # left in the caches by the previous call; only the attention launch is timed
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_steps)]
+        for s_, e in cev:
+            scratch.fill_(1)
+            s_.record(stream)
+            step()
+            e.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = [s_.elapsed_time(e) for s_, e in cev]
+        cold = {"median_ms": round(float(np.median(cold_ms)), 5),
+                "p10_ms": round(float(np.percentile(cold_ms, 10)), 5),
+                "p90_ms": round(float(np.percentile(cold_ms, 90)), 5),
+                "calls": args.cold_steps}
+        del scratch
+        log(f"[bench] cold (512 MiB written between calls): median {cold['median_ms']:.4f} ms")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -521,7 +552,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
                    "causal": w.causal, "seed": w.seed,
-                   "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
+                   "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+                   "launch_ms": launch_stats, "cold": cold, "versions": versions(torch)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

@@ -122,6 +122,11 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
   if (((size_t)Nq + 256) * D >= ((size_t)1 << 31) || ((size_t)Nk + 256) * D >= ((size_t)1 << 31))
     return ATTN_ERR_TOO_LARGE;
   attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, s_eff, causal, kv_lens);
+  // FP8: the 4-wave kernel unless the ping-pong kernel is requested explicitly.  The
+  // FP8 softmax outlasts the FP8 matrix phase, and the ping-pong lock-step then leaves
+  // the matrix cores idle (B=1 H=32 N=8192 causal: 0.402 ms against 0.360 ms).
+  if (g_bf16_kernel == ATTN_KERNEL_PINGPONG)
+    return attn89::launch_attn_fwd_fp8_pp(a, D, v_descale, (hipStream_t)stream);
   return attn89::launch_attn_fwd_fp8(a, D, v_descale, (hipStream_t)stream);
 }
 

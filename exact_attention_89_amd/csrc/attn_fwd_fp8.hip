@@ -38,16 +38,11 @@
 // the key loop is unrolled by two so every LDS offset is an immediate.
 #include <type_traits>
 
-#include "attn_bf16_tiles.hpp"
+#include "attn_fp8_tiles.hpp"
 #include "launch.hpp"
 
 namespace attn89 {
 namespace {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-constexpr float kPShift = 6.0f;   // p' = 2^6 * p
-constexpr float kSlack8 = 2.0f;   // lazy-correction slack of the FP8 kernel
 
 template <int D>
 struct Cfg8 {
@@ -64,34 +59,6 @@ struct Cfg8 {
   static constexpr int LDS = 4 * TILE;           // K double buffer, V^T double buffer
   static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
 };
-
-// K chunk swizzle (16-byte chunks): the 16 lanes the LDS serves together read one
-// chunk column of 16 consecutive rows; with 128-byte rows two rows span the banks,
-// with 64-byte rows four.  Adding 32 to the row leaves it unchanged.
-template <int D>
-__device__ __forceinline__ int kswz8(int row) {
-  return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
-}
-// V^T rows are 64 bytes (4 chunks): four rows span the banks.
-__device__ __forceinline__ int vtswz8(int d) { return (d >> 2) & 3; }
-
-__device__ __forceinline__ i32x8 lds_load32(const lds_u8* base, unsigned off) {
-  const u32x4 lo = lds_load<u32x4>(base, off);
-  const u32x4 hi = lds_load<u32x4>(base, off + 16);
-  return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
-__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  // formats 0/0: both operands E4M3; no block scales
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// the 8-byte load of 8 consecutive dimensions
-__device__ __forceinline__ u32x2 buffer_load8_so(__amdgpu_buffer_rsrc_t r, unsigned voff,
-                                                 int soff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
 
 // PRE: scale <= 0, scores are scaled before they are masked.
 template <int D, bool PRE>
@@ -133,10 +100,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
 #pragma unroll
   for (int s = 0; s < C::DSTEPS; ++s) {
     const unsigned off = (unsigned)qrow * D + 64 * s + 32 * lg;
-    const u32x4 lo = buffer_load16(qrs, off);
-    const u32x4 hi = buffer_load16(qrs, off + 16);
-    qf[s] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    qf[s] = join32(buffer_load16(qrs, off), buffer_load16(qrs, off + 16));
   }
 
   // ---- K: global -> LDS without registers (swizzled row-major) ----
@@ -185,16 +149,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     if (v_owner) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        // 4 x 4 byte transpose: keys 0..3 (vreg[k][i]) x dimensions 4i .. 4i+3
-        const unsigned w0 = vreg[0][i], w1 = vreg[1][i], w2 = vreg[2][i], w3 = vreg[3][i];
-        const unsigned lo01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
-        const unsigned hi01 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
-        const unsigned lo23 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
-        const unsigned hi23 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
-        const unsigned d4[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
-                                __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
-                                __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
-                                __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+        const u32x4 d4 = transpose4x4_bytes(vreg[0][i], vreg[1][i], vreg[2][i], vreg[3][i]);
 #pragma unroll
         for (int x = 0; x < 4; ++x)
           *(__attribute__((address_space(3))) unsigned*)(
@@ -222,10 +177,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const lds_u8* base = lds + stage * C::TILE + kb * 32 * C::ROWB;
-        const u32x4 lo = lds_load<u32x4>(base, kro[s][0]);
-        const u32x4 hi = lds_load<u32x4>(base, kro[s][1]);
-        const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const i32x8 a = join32(lds_load<u32x4>(base, kro[s][0]), lds_load<u32x4>(base, kro[s][1]));
         sacc[kb] = mfma_fp8(a, qf[s], s == 0 ? (f32x16){} : sacc[kb]);
       }
   };
@@ -292,24 +244,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        float e[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          e[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][4 * w + x], c_exp, -m_sh));
-        lsum += (e[0] + e[1]) + (e[2] + e[3]);
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
-        pf[4 * kb + w] = word;
+        pf[4 * kb + w] = exp2_pack_e4m3(scur[kb][4 * w], scur[kb][4 * w + 1], scur[kb][4 * w + 2],
+                                        scur[kb][4 * w + 3], c_exp, m_sh, lsum);
       }
     l_run += lsum;
     // O^T += V^T P^T
 #pragma unroll
     for (int d = 0; d < C::DBLK; ++d) {
       const lds_u8* base = lds + C::VT0 + PAR * C::TILE + d * 32 * C::VTROWB;
-      const u32x4 lo = lds_load<u32x4>(base, vro[0]);
-      const u32x4 hi = lds_load<u32x4>(base, vro[1]);
-      const i32x8 va = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const i32x8 va = join32(lds_load<u32x4>(base, vro[0]), lds_load<u32x4>(base, vro[1]));
       oacc[d] = mfma_fp8(va, pf, oacc[d]);
     }
     if (!LAST) {

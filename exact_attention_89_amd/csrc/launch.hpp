@@ -29,6 +29,8 @@ int launch_attn_fwd_f32(const FwdArgs& a, int D, hipStream_t stream);
 // FP8 (E4M3) forward, 4-wave workgroups; c_exp / c_pre carry scale * q_descale *
 // k_descale, v_descale multiplies the output.
 int launch_attn_fwd_fp8(const FwdArgs& a, int D, float v_descale, hipStream_t stream);
+// the same in 8-wave ping-pong workgroups of 256 rows
+int launch_attn_fwd_fp8_pp(const FwdArgs& a, int D, float v_descale, hipStream_t stream);
 
 // Workspace layout of the materialised baseline: S (fp32) then P (bf16), both
 // [B][H][Nq][ld] with ld = Nk rounded up to a multiple of 64.

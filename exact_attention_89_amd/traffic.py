@@ -66,8 +66,9 @@ def _decode_hash():
 
 
 def _fp8_hash():
-    """Sources of the FP8 fused forward."""
-    return _hash(("attn_fwd_fp8.hip", "attn_bf16_tiles.hpp", "common.hpp"))
+    """Sources of the FP8 fused forward kernels."""
+    return _hash(("attn_fwd_fp8.hip", "attn_fwd_fp8_pp.hip", "attn_fp8_tiles.hpp",
+                  "attn_bf16_tiles.hpp", "common.hpp"))
 
 
 def _softmax_hash():

@@ -75,17 +75,19 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const int32_t* kv_lens, void* stream);
 
 /*
- * attn_fwd_select_kernel -- which of the two bf16 forward kernels attn_fwd
- * launches.  Both compute the same function with the same arithmetic (bitwise
- * identical results); they differ only in how work is spread over the GPU:
+ * attn_fwd_select_kernel -- which of the two forward kernels attn_fwd (bf16) and
+ * attn_fwd_fp8 (E4M3) launch.  For each input type both kernels compute the same
+ * function with the same arithmetic (bitwise identical results); they differ only in
+ * how work is spread over the GPU:
  *
  *   ATTN_KERNEL_PINGPONG  8-wave workgroups of 256 query rows, two wave groups
  *                         half a key tile apart (one on the matrix cores while
  *                         the other computes its softmax); one workgroup per CU
  *   ATTN_KERNEL_FOURWAVE  4-wave workgroups of 128 query rows, two per CU
- *   ATTN_KERNEL_AUTO      (default) ping-pong when D = 128, Nq >= 256 and its
- *                         grid, ceil(Nq/256)*B*H workgroups, covers every
- *                         compute unit; otherwise four-wave
+ *   ATTN_KERNEL_AUTO      (default) attn_fwd: ping-pong when D = 128, Nq >= 256
+ *                         and its grid, ceil(Nq/256)*B*H workgroups, covers every
+ *                         compute unit, otherwise four-wave; attn_fwd_fp8:
+ *                         four-wave (the faster one for FP8 at every measured shape)
  *
  * The setting is process-wide and not synchronised: change it only while no
  * other thread calls attn_fwd.  Returns the previous setting, or

@@ -34,6 +34,17 @@ def _say(msg):
     sys.stdout.flush()
 
 
+@pytest.fixture(params=["pingpong", "fourwave"])
+def fp8_kernel(request):
+    """Run an FP8 test on each of the two FP8 forward kernels (forced, not auto-picked)."""
+    which = {"pingpong": api.ATTN_KERNEL_PINGPONG,
+             "fourwave": api.ATTN_KERNEL_FOURWAVE}[request.param]
+    prev = api.attn_fwd_select_kernel(which)
+    _say(f"[fp8] kernel: {request.param}")
+    yield request.param
+    api.attn_fwd_select_kernel(prev)
+
+
 def _dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
@@ -67,35 +78,35 @@ def _run(B, H, Nq, Nk, D, causal=False, lens=None, seed=0, std=1.0, scale=None, 
                                    (300, 300), (513, 130)])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_shapes(Nq, Nk, D, causal):
+def test_fp8_shapes(Nq, Nk, D, causal, fp8_kernel):
     _run(2, 3, Nq, Nk, D, causal, seed=Nq * 7 + Nk + D + int(causal))
 
 
 @pytest.mark.parametrize("causal,lens", [(False, [0, 1, 65, 700]), (False, [-3, 64, 129, 2000]),
                                          (True, [700, 0, 5, 64]), (True, None)])
 @pytest.mark.parametrize("D", [64, 128])
-def test_fp8_kv_lens(causal, lens, D):
+def test_fp8_kv_lens(causal, lens, D, fp8_kernel):
     _run(4, 2, 700, 700, D, causal, lens=lens, seed=11 + D)
 
 
 @pytest.mark.parametrize("std", [0.25, 2.0, 4.0])
-def test_fp8_peaked_and_flat_rows(std):
+def test_fp8_peaked_and_flat_rows(std, fp8_kernel):
     """Larger std gives peaked rows (one key dominates), smaller nearly uniform rows."""
     _run(1, 4, 256, 1024, 128, True, seed=5, std=std)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.2, 1.5])
-def test_fp8_scale_values(scale):
+def test_fp8_scale_values(scale, fp8_kernel):
     """scale <= 0 takes the pre-scaled instantiation; 0 gives the mean of valid values."""
     _run(2, 2, 130, 260, 128, False, lens=[260, 100], seed=3, scale=scale)
 
 
-def test_fp8_descales_not_amax():
+def test_fp8_descales_not_amax(fp8_kernel):
     """Descales need not come from amax: any positive factors are honoured."""
     _run(1, 2, 200, 200, 128, True, seed=8, ds=(0.03125, 0.0078125, 3.0))
 
 
-def test_fp8_zero_query():
+def test_fp8_zero_query(fp8_kernel):
     """q = 0: every valid key weighs the same, O = mean of the values, LSE = ln(#keys)."""
     q8, k8, v8, ds = random_fp8_case(4, 1, 2, 100, 300, 64)
     q8[:] = 0
@@ -106,13 +117,30 @@ def test_fp8_zero_query():
     assert np.max(np.abs(o - mean)) <= 2.0 ** -8 * np.max(np.abs(mean)) + 1e-5
 
 
-def test_fp8_single_key_is_exact():
+def test_fp8_single_key_is_exact(fp8_kernel):
     """Nk = 1: the one weight is 2^6 (exact), O = the dequantised value row in bf16."""
     q8, k8, v8, ds = random_fp8_case(9, 2, 2, 40, 1, 128)
     o, _ = _gpu_fp8(q8, k8, v8, ds, 0.1, False, None)
     ref = np.broadcast_to(oracle.dequantize(v8, ds[2]), o.shape)
     bf16 = torch.from_numpy(np.ascontiguousarray(ref, dtype=np.float32)).to(torch.bfloat16)
     assert np.array_equal(o, bf16.float().numpy())
+
+
+@pytest.mark.parametrize("B,H,N,D,causal,lens", [
+    (1, 4, 300, 128, True, None), (2, 3, 513, 128, False, [513, 77]), (1, 2, 1000, 64, True, None),
+    (2, 2, 256, 64, False, [0, 200])])
+def test_fp8_both_kernels_bitwise_equal(B, H, N, D, causal, lens):
+    """The two FP8 kernels run the same per-wave arithmetic in the same order."""
+    q8, k8, v8, ds = random_fp8_case(N + D, B, H, N, N, D)
+    out = []
+    for which in (api.ATTN_KERNEL_PINGPONG, api.ATTN_KERNEL_FOURWAVE):
+        prev = api.attn_fwd_select_kernel(which)
+        try:
+            _say(f"[fp8] kernel {which} {B}x{H}x{N}x{D} causal={causal} lens={lens}")
+            out.append(_gpu_fp8(q8, k8, v8, ds, D ** -0.5, causal, lens))
+        finally:
+            api.attn_fwd_select_kernel(prev)
+    assert np.array_equal(out[0][0], out[1][0]) and np.array_equal(out[0][1], out[1][1])
 
 
 def test_fp8_deterministic():
