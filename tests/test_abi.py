@@ -161,3 +161,36 @@ def test_splitkv_plan_and_checks(lib):
     assert lib.attn_fwd_splitkv(*args, p, need - 1, None) == -6
     assert lib.attn_fwd_splitkv(*args, None, need, None) == -6
     assert lib.attn_fwd_splitkv(None, *args[1:], p, need, None) == -1
+
+
+def test_headers_compile_and_link_as_c(tmp_path, lib):
+    """A C99 program (gcc, -Wall -Wextra -pedantic -Werror) includes both headers,
+    takes the address of every declared function (so the linker resolves each one
+    against libattn89.so) and calls the host-side checks: the boundary is plain C."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    names = _declared()
+    src = tmp_path / "abi.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"attn.h\"\n#include \"softmax_rows.h\"\n"
+        "typedef void (*fn_t)(void);\n"
+        "static const fn_t all[] = {" + ", ".join(f"(fn_t){n}" for n in names) + "};\n"
+        "int main(void) {\n"
+        "  int st = attn_fwd(NULL, NULL, NULL, NULL, NULL, 1, 1, 1, 1, 64, 0.125f, 0, NULL, NULL);\n"
+        "  int st2 = softmax_rows_f32(NULL, NULL, 1, 1, NULL);\n"
+        "  printf(\"%d %d %d %u\\n\", attn_abi_version(), st, st2, (unsigned)(sizeof all / sizeof *all));\n"
+        "  return (st == ATTN_ERR_NULL && st2 == ATTN_ERR_NULL) ? 0 : 1;\n}\n")
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(api.library_path())
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+           "-Wno-cast-function-type", "-I", os.path.join(ROOT, "include"), str(src),
+           "-L", libdir, "-l:libattn89.so", f"-Wl,-rpath,{libdir}",
+           "-Wl,-rpath-link,/opt/rocm/lib", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.split() == ["2", "-1", "-1", str(len(names))]
