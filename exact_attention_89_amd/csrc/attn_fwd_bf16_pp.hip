@@ -325,8 +325,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
 
   // One tile period of group G; PAR = t & 1 selects the buffers at compile time.
   //   MFMA phase:    O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
-  //   softmax phase: P(t); G0 writes V(t) to V^T buffer PAR and requests V(t+1),
-  //                  G1 requests K(t+2) into K buffer PAR
+  //   softmax phase: G0 writes V(t) to V^T buffer PAR and requests V(t+1), G1
+  //                  requests K(t+2) into K buffer PAR; then P(t)
   auto period = [&](const int t, auto grp_tag, auto par_tag, auto first_tag)
                     __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
@@ -339,13 +339,15 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     if (G == 1) wait_vm0();   // K(t+1) has landed: it is read after the barrier
     phase_barrier();
     valu_priority();
-    softmax(t);
+    // data movement first: the V^T writes then drain while the exponentials run
+    // instead of at the barrier (V^T buffer PAR was last read by P.V(t-2))
     if (G == 0) {
       store_v(PAR);
       if (t + 1 < n_tiles) load_v(t + 1);
     } else {
       if (t + 2 < n_tiles) load_k(t + 2, PAR);
     }
+    softmax(t);
     phase_barrier();
   };
 
