@@ -29,6 +29,12 @@
 // swizzled K and V^T tiles) and the lazy online correction are described in
 // attn_bf16_tiles.hpp.
 //
+// Masking.  The leading key tiles that every row of the workgroup sees whole run a
+// copy of the loop body with no mask code and no mask test; only the tiles at the
+// causal diagonal or the key-length tail take the body that checks, per wave, whether
+// the tile needs masking.  Scalar control flow in the softmax phase is not free: this
+// split alone is worth about 2 % at the causal headline shape.
+//
 // Data movement.  G1 moves K tiles from global memory straight into LDS
 // (buffer_load ... lds, no staging registers), row-major; G0 loads V tiles into
 // registers and writes them transposed ([D][64 keys]) during its softmax phase.
@@ -134,6 +140,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   const int q_hi = min(q0 + C::BR, p.Nq);
   const int kv_end = p.causal ? min(L, q_hi) : L;    // keys any row of the block sees
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  // leading tiles whose keys are all visible to every row of the block
+  const int n_full = PRE ? 0 : min(L, p.causal ? q0 + 1 : L) / C::BC;
   const int qw = q0 + wave * 32;                     // first row of this wave
   const int qrow = qw + lq;
 
@@ -250,17 +258,19 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
 
   // softmax of tile t: mask, row maxima -> exponent reference, lazy correction of
   // O and l, P = exp2(s*c - m) rounded to bf16 in the B-operand layout of P.V.
-  auto softmax = [&](int t) __attribute__((always_inline)) {
+  auto softmax = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
     const int j0 = t * C::BC;
-    if (PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw)) {
+    if (MASKED && (PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw))) {
+      // key j0 + off of this lane is visible iff off < lim (kv_len and causal bounds)
+      const int lim = min(L, p.causal ? qrow + 1 : L) - j0 - 8 * lg;
 #pragma unroll
       for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + kb * 32 + 16 * (r >> 3) + 8 * lg + (r & 7);
-          const bool ok = (key < L) & (!p.causal | (key <= qrow));
+          const int off = kb * 32 + 16 * (r >> 3) + (r & 7);
           const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
-          sacc[kb][r] = ok ? x : kNegInf;
+          sacc[kb][r] = off < lim ? x : kNegInf;
         }
     }
     // guard: a row with no valid key so far keeps m = -inf and uses 0 as its
@@ -274,7 +284,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     const bool move = mx > m_run + kRescaleSlack;
     const float m_new = move ? mx : m_run;
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    if (__any(move)) {
+    if (__builtin_expect(__any(move), 0)) {
       const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
       l_run *= alpha;
 #pragma unroll
@@ -327,7 +337,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   //   MFMA phase:    O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
   //   softmax phase: G0 writes V(t) to V^T buffer PAR and requests V(t+1), G1
   //                  requests K(t+2) into K buffer PAR; then P(t)
-  auto period = [&](const int t, auto grp_tag, auto par_tag, auto first_tag)
+  auto period = [&](const int t, auto grp_tag, auto par_tag, auto first_tag, auto mask_tag)
                     __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
@@ -347,7 +357,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     } else {
       if (t + 2 < n_tiles) load_k(t + 2, PAR);
     }
-    softmax(t);
+    softmax(t, mask_tag);
     phase_barrier();
   };
 
@@ -371,13 +381,20 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
         if (n_tiles > 1) load_k(1, 1);
         phase_barrier();
       }
-      period(0, grp_tag, I0{}, std::true_type{});
+      using T_ = std::true_type;
+      using F_ = std::false_type;
+      period(0, grp_tag, I0{}, T_{}, T_{});
       int t = 1;
-      for (; t + 1 < n_tiles; t += 2) {
-        period(t, grp_tag, I1{}, std::false_type{});
-        period(t + 1, grp_tag, I0{}, std::false_type{});
+      // tiles every row of the workgroup sees whole: no mask code at all
+      for (; t + 1 < n_full; t += 2) {
+        period(t, grp_tag, I1{}, F_{}, F_{});
+        period(t + 1, grp_tag, I0{}, F_{}, F_{});
       }
-      if (t < n_tiles) period(t, grp_tag, I1{}, std::false_type{});
+      for (; t + 1 < n_tiles; t += 2) {
+        period(t, grp_tag, I1{}, F_{}, T_{});
+        period(t + 1, grp_tag, I0{}, F_{}, T_{});
+      }
+      if (t < n_tiles) period(t, grp_tag, I1{}, F_{}, T_{});
       // last MFMA phase: O += V(n-1) P(n-1)
       mfma_priority();
       if ((n_tiles - 1) & 1) pv(1);

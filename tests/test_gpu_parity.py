@@ -248,6 +248,39 @@ def test_both_kernels_bitwise_equal(B, H, N, D, causal, lens):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("B,H,Nq,Nk,D,causal,lens,scale", [
+    (1, 2, 1300, 1300, 128, True, None, None),      # six 256-row blocks, growing interiors
+    (2, 2, 777, 1500, 128, True, [1500, 900], None),  # Nq < Nk, causal and key lengths
+    (2, 1, 1500, 700, 128, True, [650, 3], None),     # Nq > Nk: rows past every key
+    (1, 2, 600, 1000, 128, False, [777], None),       # key-length tail inside a tile
+    (1, 1, 513, 513, 128, True, None, -0.05),         # scale <= 0: every tile checked
+    (1, 1, 520, 520, 64, True, [300], None)])
+def test_both_kernels_bitwise_equal_interior_split(B, H, Nq, Nk, D, causal, lens, scale):
+    """The ping-pong kernel runs the key tiles every row of a workgroup sees whole
+    without mask code and the rest with it; the four-wave kernel checks every tile.
+    Equal bits on shapes that move that boundary show the split masks nothing it
+    should keep and keeps nothing it should mask."""
+    q, k, v, lens = random_case(Nq + 7 * Nk + D, B, H, Nq, Nk, D, "bf16", lens)
+    qd, kd, vd = (_dev(x, "bf16") for x in (q, k, v))
+    ld = _lens_dev(lens)
+    out = {}
+    for which in (api.ATTN_KERNEL_PINGPONG, api.ATTN_KERNEL_FOURWAVE):
+        prev = api.attn_fwd_select_kernel(which)
+        try:
+            _say(f"[gpu] kernel {which} {B}x{H}x{Nq}x{Nk}x{D} causal={causal} lens={lens} "
+                 f"scale={scale}")
+            out[which] = api.attn_fwd(qd, kd, vd, scale=scale, causal=causal, kv_lens=ld)
+            torch.cuda.synchronize()
+        finally:
+            api.attn_fwd_select_kernel(prev)
+    (o1, l1), (o2, l2) = out.values()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    sc = D ** -0.5 if scale is None else scale
+    o_ref, lse_ref = oracle.attention_oracle(q, k, v, sc, causal=causal, kv_lens=lens)
+    check(o1.float().cpu().numpy(), l1.cpu().numpy(), o_ref, lse_ref, "bf16",
+          f"interior split {B}x{H}x{Nq}x{Nk}x{D}")
+
+
 def test_key_permutation_invariance():
     """Without a causal mask, permuting (k_j, v_j) jointly changes O only by rounding."""
     q, k, v, _ = random_case(5, 1, 2, 256, 512, 128)
