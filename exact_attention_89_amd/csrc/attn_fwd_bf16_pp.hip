@@ -52,6 +52,8 @@
 namespace attn89 {
 namespace {
 
+constexpr int kXcds = 8;   // XCDs of an MI355X
+
 template <int D>
 struct Cfg {
   static constexpr int BR = 256;                 // query rows per workgroup
@@ -119,14 +121,26 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   const int lq = lane & 31;      // query column inside the wave's 32 rows
   const int lg = lane >> 5;      // half of the wave
 
-  // Schedule: consecutive workgroups take different (b, h) of the same query block,
-  // heaviest (last, for causal) query blocks first.  Workgroups are dispatched to
-  // the 8 XCDs round robin, so when B*H is a multiple of 8 every query block of a
-  // head lands on the same XCD and its K/V re-reads stay in that XCD's L2.
+  // Schedule.  Workgroups are dispatched to the 8 XCDs round robin (workgroup i runs
+  // on XCD i mod 8), so when B*H is a multiple of 8 every query block of a head lands
+  // on one XCD and its K/V re-reads can stay in that XCD's L2.
+  //  * causal: consecutive workgroups take different (b, h) of the same query block,
+  //    heaviest (last) blocks first; the blocks of a head differ in length, and this
+  //    longest-first order is what keeps the CUs evenly loaded;
+  //  * otherwise every block of a head has the same length, and each XCD takes its
+  //    heads one at a time (all query blocks of one head, then the next), so the
+  //    K/V of only a few heads is live in its L2 at once.
   const int BH = p.B * p.H;
   const int n_qb = (p.Nq + C::BR - 1) / C::BR;
-  const int qb = n_qb - 1 - (int)blockIdx.x / BH;
-  const int bh = (int)blockIdx.x % BH;
+  int qb, bh;
+  if (!p.causal && BH % kXcds == 0) {
+    const int x = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    bh = x + kXcds * (slot / n_qb);
+    qb = n_qb - 1 - slot % n_qb;
+  } else {
+    qb = n_qb - 1 - (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x % BH;
+  }
   const int b = bh / p.H;
 
   const unsigned short* qp = (const unsigned short*)p.q + (size_t)bh * p.Nq * D;

@@ -254,12 +254,17 @@ def test_both_kernels_bitwise_equal(B, H, N, D, causal, lens):
     (2, 1, 1500, 700, 128, True, [650, 3], None),     # Nq > Nk: rows past every key
     (1, 2, 600, 1000, 128, False, [777], None),       # key-length tail inside a tile
     (1, 1, 513, 513, 128, True, None, -0.05),         # scale <= 0: every tile checked
-    (1, 1, 520, 520, 64, True, [300], None)])
+    (1, 1, 520, 520, 64, True, [300], None),
+    (2, 4, 700, 700, 128, False, [700, 333], None),   # B*H = 8: head-by-head order
+    (1, 16, 600, 900, 128, False, None, None),         # B*H = 16, two heads per XCD
+    (4, 4, 300, 300, 64, False, [0, 1, 299, 300], None)])
 def test_both_kernels_bitwise_equal_interior_split(B, H, Nq, Nk, D, causal, lens, scale):
     """The ping-pong kernel runs the key tiles every row of a workgroup sees whole
     without mask code and the rest with it; the four-wave kernel checks every tile.
     Equal bits on shapes that move that boundary show the split masks nothing it
-    should keep and keeps nothing it should mask."""
+    should keep and keeps nothing it should mask.  The non-causal cases with B*H a
+    multiple of 8 take the ping-pong kernel's head-by-head workgroup order: a block
+    it skipped or ran twice would show here too."""
     q, k, v, lens = random_case(Nq + 7 * Nk + D, B, H, Nq, Nk, D, "bf16", lens)
     qd, kd, vd = (_dev(x, "bf16") for x in (q, k, v))
     ld = _lens_dev(lens)
