@@ -33,7 +33,7 @@
 // copy of the loop body with no mask code and no mask test; only the tiles at the
 // causal diagonal or the key-length tail take the body that checks, per wave, whether
 // the tile needs masking.  Scalar control flow in the softmax phase is not free: this
-// split alone is worth about 2 % at the causal headline shape.
+// split alone is worth about 2 % at B=1 H=32 N=8192 D=128, causal.
 //
 // Data movement.  G1 moves K tiles from global memory straight into LDS
 // (buffer_load ... lds, no staging registers), row-major; G0 loads V tiles into
