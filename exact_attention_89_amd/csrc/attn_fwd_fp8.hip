@@ -73,11 +73,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
   const int lq = lane & 31;
   const int lg = lane >> 5;
 
-  // heaviest query blocks first; consecutive workgroups take different (b, h)
+  // causal: heaviest query blocks first, consecutive workgroups take different (b, h);
+  // otherwise each of the 8 XCDs takes its heads one at a time (see the bf16 kernel)
   const int BH = p.B * p.H;
   const int n_qb = (p.Nq + C::BR - 1) / C::BR;
-  const int qb = n_qb - 1 - (int)blockIdx.x / BH;
-  const int bh = (int)blockIdx.x % BH;
+  int qb, bh;
+  if (!p.causal && BH % 8 == 0) {
+    const int x = (int)blockIdx.x % 8, slot = (int)blockIdx.x / 8;
+    bh = x + 8 * (slot / n_qb);
+    qb = n_qb - 1 - slot % n_qb;
+  } else {
+    qb = n_qb - 1 - (int)blockIdx.x / BH;
+    bh = (int)blockIdx.x % BH;
+  }
   const int b = bh / p.H;
 
   const unsigned char* qp = (const unsigned char*)p.q + (size_t)bh * p.Nq * D;
@@ -91,6 +99,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
   const int q_hi = min(q0 + C::BR, p.Nq);
   const int kv_end = p.causal ? min(L, q_hi) : L;
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  // leading tiles whose keys are all visible to every row of the block
+  const int n_full = PRE ? 0 : min(L, p.causal ? q0 + 1 : L) / C::BC;
   const int qw = q0 + wave * 32;
   const int qrow = qw + lq;
 
@@ -187,15 +197,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     return PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw);
   };
   auto apply_mask = [&](int t, f32x16* sacc) {
-    const int j0 = t * C::BC;
+    // key j0 + off of this lane is visible iff off < lim (kv_len and causal bounds)
+    const int lim = min(L, p.causal ? qrow + 1 : L) - t * C::BC - 4 * lg;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        const bool ok = (key < L) & (!p.causal | (key <= qrow));
+        const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
         const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
-        sacc[kb][r] = ok ? x : kNegInf;
+        sacc[kb][r] = off < lim ? x : kNegInf;
       }
   };
 
@@ -206,16 +216,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
   float l_run = 0.f;
   const float c_exp = p.c_exp;
 
-  auto iteration = [&](const int t, auto par_tag, auto last_tag) {
+  auto iteration = [&](const int t, auto par_tag, auto last_tag, auto mask_tag) {
     constexpr int PAR = decltype(par_tag)::value;
     constexpr bool LAST = decltype(last_tag)::value;
+    constexpr bool MASKED = decltype(mask_tag)::value;
     if (!LAST) {
       load_k(t + 1, PAR ^ 1);
       load_v(t + 1);
     }
     f32x16 scur[2];
     qk(PAR, scur);
-    if (needs_mask(t)) apply_mask(t, scur);
+    if (MASKED && needs_mask(t)) apply_mask(t, scur);
     // row maximum and exponent reference (guard: a row without a valid key so far
     // keeps m = -inf and uses 0 as its reference)
     float mx = kNegInf;
@@ -227,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     const bool move = mx > m_run + kSlack8;
     const float m_new = move ? mx : m_run;
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    if (__any(move)) {
+    if (__builtin_expect(__any(move), 0)) {
       const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
       l_run *= alpha;
 #pragma unroll
@@ -268,16 +279,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
   if (n_tiles > 0) store_v(0);
   __syncthreads();
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   int t = 0;
+  // tiles every row of the workgroup sees whole: no mask code at all
+  for (; t + 2 < n_tiles && t + 1 < n_full; t += 2) {
+    iteration(t, I0{}, F_{}, F_{});
+    iteration(t + 1, I1{}, F_{}, F_{});
+  }
   for (; t + 2 < n_tiles; t += 2) {
-    iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
-    iteration(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    iteration(t, I0{}, F_{}, T_{});
+    iteration(t + 1, I1{}, F_{}, T_{});
   }
   if (t + 1 < n_tiles) {
-    iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
-    iteration(t + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    iteration(t, I0{}, F_{}, T_{});
+    iteration(t + 1, I1{}, T_{}, T_{});
   } else if (t < n_tiles) {
-    iteration(t, std::integral_constant<int, 0>{}, std::true_type{});
+    iteration(t, I0{}, T_{}, T_{});
   }
 
   // ---- epilogue: O = v_descale * a / l (0 without a valid key), LSE ----
