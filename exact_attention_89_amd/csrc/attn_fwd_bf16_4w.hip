@@ -85,16 +85,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   const int lq = lane & 31;   // query column inside the wave's 32 rows
   const int lg = lane >> 5;   // half of the wave
 
-  // Schedule: consecutive workgroups take different (b, h) of the same query block,
-  // heaviest (last, for causal) query blocks first.  Workgroups are dispatched to
-  // the 8 XCDs round robin, so when B*H is a multiple of 8 every query block of a
-  // head lands on the same XCD and its K/V re-reads stay in that XCD's L2.
+  // Schedule.  Workgroups are dispatched to the 8 XCDs round robin, so when B*H is a
+  // multiple of 8 every query block of a head lands on one XCD and its K/V re-reads
+  // can stay in that XCD's L2.  Causal (or split-key) calls: consecutive workgroups
+  // take different (b, h) of the same query block, heaviest (last) blocks first,
+  // which balances blocks of unequal length.  Otherwise every block of a head has the
+  // same length and each XCD takes its heads one at a time, all query blocks of one
+  // head before the next, so few heads' K/V compete for its L2.
   const int BH = p.B * p.H;
   const int n_qb = (p.Nq + C::BR - 1) / C::BR;
   const int split = SPLIT ? (int)blockIdx.x % p.n_splits : 0;
   const int wg_id = SPLIT ? (int)blockIdx.x / p.n_splits : (int)blockIdx.x;
-  const int qb = n_qb - 1 - wg_id / BH;
-  const int bh = wg_id % BH;
+  int qb, bh;
+  if (!SPLIT && !p.causal && BH % 8 == 0) {
+    const int x = wg_id % 8, slot = wg_id / 8;
+    bh = x + 8 * (slot / n_qb);
+    qb = n_qb - 1 - slot % n_qb;
+  } else {
+    qb = n_qb - 1 - wg_id / BH;
+    bh = wg_id % BH;
+  }
   const int b = bh / p.H;
 
   // rows of this (batch, head): nq queries and L valid keys, ld elements apart
