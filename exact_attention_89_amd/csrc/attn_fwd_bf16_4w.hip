@@ -141,6 +141,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   // key tiles [t_begin, n_tiles) of this workgroup (all of them unless split)
   const int t_begin = SPLIT ? split * (p.kv_chunk / C::BC) : 0;
   const int n_tiles = SPLIT ? min(n_tiles_all, t_begin + p.kv_chunk / C::BC) : n_tiles_all;
+  // leading tiles whose keys are all visible to every row of the block
+  const int n_full = PRE ? 0 : min(L, p.causal ? q0 + 1 : L) / C::BC;
   const int qw = q0 + wave * 32;                     // first row of this wave
   const int qrow = qw + lq;
 
@@ -240,15 +242,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     return PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw);
   };
   auto apply_mask = [&](int t, f32x16* sacc) {
-    const int j0 = t * C::BC;
+    // key j0 + off of this lane is visible iff off < lim (kv_len and causal bounds)
+    const int lim = min(L, p.causal ? qrow + 1 : L) - t * C::BC - 8 * lg;
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j0 + kb * 32 + 16 * (r >> 3) + 8 * lg + (r & 7);
-        const bool ok = (key < L) & (!p.causal | (key <= qrow));
+        const int off = kb * 32 + 16 * (r >> 3) + (r & 7);
         const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
-        sacc[kb][r] = ok ? x : kNegInf;
+        sacc[kb][r] = off < lim ? x : kNegInf;
       }
   };
 
@@ -261,7 +263,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   const float c_exp = p.c_exp;
 
   // ---- one key tile; PAR = t & 1 selects the buffers at compile time ----
-  auto iteration = [&](const int t, auto par_tag, auto last_tag) {
+  auto iteration = [&](const int t, auto par_tag, auto last_tag, auto mask_tag) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
     constexpr bool LAST = decltype(last_tag)::value;
     // a) prefetch the next tile
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     // b) scores; c) mask
     f32x16 scur[C::KBLK];
     qk(PAR, scur);
-    if (needs_mask(t)) apply_mask(t, scur);
+    if (MASKED && needs_mask(t)) apply_mask(t, scur);
     // d) row maximum (in-lane, then with the partner lane) and the new reference;
     //    guard: a row with no valid key so far keeps m = -inf and uses 0 as its
     //    exponent reference, so no -inf - (-inf) is ever formed
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     const bool move = mx > m_run + kRescaleSlack;
     const float m_new = move ? mx : m_run;
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    if (__any(move)) {
+    if (__builtin_expect(__any(move), 0)) {
       const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
       l_run *= alpha;
 #pragma unroll
@@ -341,16 +344,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
   if (n_tiles > t_begin) store_v(0);
   __syncthreads();
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   int t = t_begin;
+  // tiles every row of the workgroup sees whole: no mask code at all
+  for (; t + 2 < n_tiles && t + 1 < n_full; t += 2) {
+    iteration(t, I0{}, F_{}, F_{});
+    iteration(t + 1, I1{}, F_{}, F_{});
+  }
   for (; t + 2 < n_tiles; t += 2) {
-    iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
-    iteration(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    iteration(t, I0{}, F_{}, T_{});
+    iteration(t + 1, I1{}, F_{}, T_{});
   }
   if (t + 1 < n_tiles) {
-    iteration(t, std::integral_constant<int, 0>{}, std::false_type{});
-    iteration(t + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    iteration(t, I0{}, F_{}, T_{});
+    iteration(t + 1, I1{}, T_{}, T_{});
   } else if (t < n_tiles) {
-    iteration(t, std::integral_constant<int, 0>{}, std::true_type{});
+    iteration(t, I0{}, T_{}, T_{});
   }
 
   // ---- epilogue: O = a / l (0 for rows with no valid key), LSE = ln2 (m + log2 l) ----
