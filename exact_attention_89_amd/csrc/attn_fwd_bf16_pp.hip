@@ -33,7 +33,10 @@
 // copy of the loop body with no mask code and no mask test; only the tiles at the
 // causal diagonal or the key-length tail take the body that checks, per wave, whether
 // the tile needs masking.  Scalar control flow in the softmax phase is not free: this
-// split alone is worth about 2 % at B=1 H=32 N=8192 D=128, causal.
+// split alone is worth about 2 % at B=1 H=32 N=8192 D=128, causal.  On those boundary
+// tiles a wave none of whose rows sees any key of the tile (the causal diagonal block,
+// the key-length tail) skips that tile's products and softmax, whose contributions
+// would be exact zeros; it still moves data and meets every barrier.
 //
 // Data movement.  G1 moves K tiles from global memory straight into LDS
 // (buffer_load ... lds, no staging registers), row-major; G0 loads V tiles into
@@ -351,15 +354,36 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   //   MFMA phase:    O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
   //   softmax phase: G0 writes V(t) to V^T buffer PAR and requests V(t+1), G1
   //                  requests K(t+2) into K buffer PAR; then P(t)
+  // true when no row of this wave sees any key of tile t (wave-uniform)
+  auto wave_blind = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * C::BC;
+    return j0 >= L || (p.causal && j0 > qw + 31);
+  };
+
   auto period = [&](const int t, auto grp_tag, auto par_tag, auto first_tag, auto mask_tag)
                     __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
     constexpr bool FIRST = decltype(first_tag)::value;
+    constexpr bool MASKED = decltype(mask_tag)::value;
     mfma_priority();
-    if (!FIRST) pv(PAR ^ 1);
-    qk(PAR);
-    schedule_mfma_phase<FIRST ? C::DSTEPS * C::KBLK : 2 * C::DSTEPS * C::KBLK>();
+    if (MASKED) {
+      // boundary tiles: a tile none of whose keys this wave's rows see adds exact
+      // zeros to O and l, so its products and softmax are skipped (loads and
+      // barriers still run: the other waves need the tiles)
+      if (!FIRST && !wave_blind(t - 1)) {
+        pv(PAR ^ 1);
+        schedule_mfma_phase<C::DSTEPS * C::KBLK>();
+      }
+      if (!wave_blind(t)) {
+        qk(PAR);
+        schedule_mfma_phase<C::DSTEPS * C::KBLK>();
+      }
+    } else {
+      if (!FIRST) pv(PAR ^ 1);
+      qk(PAR);
+      schedule_mfma_phase<FIRST ? C::DSTEPS * C::KBLK : 2 * C::DSTEPS * C::KBLK>();
+    }
     if (G == 1) wait_vm0();   // K(t+1) has landed: it is read after the barrier
     phase_barrier();
     valu_priority();
@@ -371,7 +395,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     } else {
       if (t + 2 < n_tiles) load_k(t + 2, PAR);
     }
-    softmax(t, mask_tag);
+    if (!MASKED || !wave_blind(t)) softmax(t, mask_tag);
     phase_barrier();
   };
 
@@ -411,8 +435,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
       if (t < n_tiles) period(t, grp_tag, I1{}, F_{}, T_{});
       // last MFMA phase: O += V(n-1) P(n-1)
       mfma_priority();
-      if ((n_tiles - 1) & 1) pv(1);
-      else pv(0);
+      if (!wave_blind(n_tiles - 1)) {
+        if ((n_tiles - 1) & 1) pv(1);
+        else pv(0);
+      }
       valu_priority();
       // G0 ends one phase early; it meets G1's last softmax barrier
       if (G == 0) phase_barrier();
