@@ -59,7 +59,11 @@ __device__ __forceinline__ int vtswz(int d) { return (d >> 1) & 7; }
 __device__ __forceinline__ float max_with_partner(float x) {
   const unsigned u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  // the inputs are scores or -inf, never NaN: a plain v_max_f32 (fmaxf would first
+  // quiet both operands, two more instructions)
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  return m;
 }
 
 __device__ __forceinline__ float sum_with_partner(float x) {

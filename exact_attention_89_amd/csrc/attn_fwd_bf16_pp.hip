@@ -243,7 +243,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   for (int d = 0; d < C::DBLK; ++d) oacc[d] = (f32x16){};
   f32x16 sacc[C::KBLK];   // S(t), from its MFMA phase to its softmax phase
   bf16x8 pf[C::KBLK][2];  // P(t), from its softmax phase to the next MFMA phase
-  float m_run = kNegInf;  // exponent reference (log2 domain)
+  float m_run = kNegInf;  // running maximum that set the reference (log2 domain)
+  float m_use = 0.f;      // exponent reference: m_run, or 0 while m_run = -inf
+  float m_thr = kNegInf;  // (m_run + kRescaleSlack) / c_exp: raw score that moves it
   float l_run = 0.f;      // this lane's part of the running sum
   const float c_exp = p.c_exp;
 
@@ -297,19 +299,22 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = max_with_partner(mx) * c_exp;
-    const bool move = mx > m_run + kRescaleSlack;
-    const float m_new = move ? mx : m_run;
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    mx = max_with_partner(mx);
+    // compared in the raw score domain, so the common case (no move) is one compare
+    const bool move = mx > m_thr;
     if (__builtin_expect(__any(move), 0)) {
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+      const float m_new = move ? mx * c_exp : m_run;
+      const float mu = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mu) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < C::DBLK; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+      m_run = m_new;
+      m_use = mu;
+      m_thr = (m_run + kRescaleSlack) / c_exp;
     }
-    m_run = m_new;
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
