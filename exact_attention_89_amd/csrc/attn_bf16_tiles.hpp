@@ -35,8 +35,10 @@ __device__ __forceinline__ T lds_load(const lds_u8* base, unsigned off) {
 // How far (log2 units) the row maximum may rise above the exponent reference before
 // the accumulators are corrected.  Online correction, lazily: the exponent reference
 // of a row moves to the new row maximum only when the maximum exceeds it by more than
-// this; until then exponentials are taken against the older reference and stay
-// <= 2^kRescaleSlack.  Numerator and normaliser always share one reference, so a / l
+// this (the kernels compare the raw maximum with (reference + this) / (scale log2 e));
+// until then exponentials are taken against the older reference and stay at most
+// 2^kRescaleSlack, up to the rounding of that comparison.  Numerator and normaliser
+// always share one reference, so a / l
 // is the same; when the reference moves both are multiplied by
 // alpha = exp2(m_old - m_new), the correction of the recurrence.
 constexpr float kRescaleSlack = 8.0f;

@@ -355,16 +355,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   }
   };
 
-  // One tile period of group G; PAR = t & 1 selects the buffers at compile time.
-  //   MFMA phase:    O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
-  //   softmax phase: G0 writes V(t) to V^T buffer PAR and requests V(t+1), G1
-  //                  requests K(t+2) into K buffer PAR; then P(t)
   // true when no row of this wave sees any key of tile t (wave-uniform)
   auto wave_blind = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * C::BC;
     return j0 >= L || (p.causal && j0 > qw + 31);
   };
 
+  // One tile period of group G; PAR = t & 1 selects the buffers at compile time.
+  //   MFMA phase:    O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
+  //   softmax phase: G0 writes V(t) to V^T buffer PAR and requests V(t+1), G1
+  //                  requests K(t+2) into K buffer PAR; then P(t)
   auto period = [&](const int t, auto grp_tag, auto par_tag, auto first_tag, auto mask_tag)
                     __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
