@@ -60,33 +60,135 @@ def measured_traffic(workload):
     return fused.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, lens, budget_s):
-    """Time the fp64 oracle on whole heads of the workload until ``budget_s`` passes."""
+def cpu_info():
+    """Cores this process may run on and the host CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+# The oracle's inputs for the forked workers of cpu_baseline_attention: set in the parent
+# before the pool forks, inherited copy-on-write (never pickled).
+_ORACLE_INPUTS = None
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)     # one BLAS thread per worker: the pool is the parallelism
+
+
+def _cpu_oracle_chunk(task):
+    """The fp64 oracle on query rows [r0, r1) of (b, h); returns the task and its wall time."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     import oracle
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                   if i.get("user_api") == "blas"] or [1])
-    heads = 0
+    b, h, r0, r1 = task
+    q, k, v, lens, scale, causal = _ORACLE_INPUTS
+    nk = k.shape[2]
+    valid = oracle.valid_keys(r0, r1, nk, causal, oracle.kv_length(lens, b, nk))
     t0 = time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            oracle.attention_oracle(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
-                                    v[b:b + 1, h:h + 1], w.scale, causal=w.causal,
-                                    kv_lens=None if lens is None else lens[b:b + 1])
-            heads += 1
-            if time.perf_counter() - t0 >= budget_s:
+    oracle.attention_rows(np.asarray(q[b, h, r0:r1], dtype=np.float64),
+                          np.asarray(k[b, h], dtype=np.float64),
+                          np.asarray(v[b, h], dtype=np.float64),
+                          oracle.effective_scale(scale), valid)
+    return task, time.perf_counter() - t0
+
+
+def cpu_baseline_attention(w, q, k, v, lens, budget_s, chunk=1024):
+    """Time the fp64 oracle on the workload's own inputs, spread over the host's cores.
+
+    A process pool (fork; called before this process touches the GPU) with one worker per
+    core this process may use and one BLAS thread per worker takes (b, h, 1024-row) chunks
+    in order until ``budget_s`` has passed.  Each chunk is the oracle's full computation
+    for those rows (every key materialised, then masked).  ``value`` counts the metric's
+    flops for the rows done (4*Nk*D per row, halved when causal, so it compares with the
+    GPU figure); ``fp64_gflops`` counts the work the oracle really does (4*Nk*D flop per
+    row, all keys) and ``exp_per_s`` its exponentials (Nk per row)."""
+    import multiprocessing
+
+    global _ORACLE_INPUTS
+    cores, model = cpu_info()
+    _ORACLE_INPUTS = (q, k, v, lens, w.scale, w.causal)
+    tasks = [(b, h, r0, min(w.Nq, r0 + chunk))
+             for b in range(w.B) for h in range(w.H) for r0 in range(0, w.Nq, chunk)]
+    done_rows, n_done = 0, 0
+    ctx = multiprocessing.get_context("fork")
+    pool = ctx.Pool(cores, initializer=_cpu_worker_init)
+    try:
+        t0 = time.perf_counter()
+        t_last = t0
+        for (_, _, r0, r1), _dt in pool.imap_unordered(_cpu_oracle_chunk, tasks):
+            done_rows += r1 - r0
+            n_done += 1
+            t_last = time.perf_counter()
+            if t_last - t0 >= budget_s:
                 break
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    flops = w.metric_flops() / (w.B * w.H) * heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} (batch, head) pairs of {w.name}, every query "
-                      f"row, fp64 numpy oracle, {dt:.1f} s wall; flops counted as in the "
-                      f"metric"}
+    finally:
+        pool.terminate()
+        pool.join()
+        _ORACLE_INPUTS = None
+    dt = t_last - t0
+    metric_per_row = w.metric_flops() / (w.B * w.H * w.Nq)
+    real_per_row = 4.0 * w.Nk * w.D
+    return {"value": metric_per_row * done_rows / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_done} of {len(tasks)} ({chunk}-row, batch, head) chunks of {w.name} "
+                      f"({done_rows} query rows), fp64 numpy oracle in a {cores}-process pool "
+                      f"with 1 BLAS thread each, {dt:.1f} s wall; value counts the metric's "
+                      f"flops for those rows",
+            "cpu_model": model,
+            "fp64_gflops": round(real_per_row * done_rows / dt / 1e9, 3),
+            "exp_per_s": round(w.Nk * done_rows / dt, 1),
+            "rows": int(done_rows), "wall_s": round(dt, 3)}
+
+
+def check_rows(w):
+    """(b, h, i) rows on which bench.py compares the GPU output with the oracle: the first
+    and last rows and tile edges of eight (b, h) pairs spread over the batch and heads, the
+    first and last row of every batch entry (a sequence with no valid key among them when
+    the workload has one), and 48 random rows."""
+    import numpy as np
+    rng = np.random.default_rng(0xC0FFEE)
+    bh = sorted({int(x) for x in np.linspace(0, w.B * w.H - 1, num=min(8, w.B * w.H))})
+    edges = [0, 1, 63, 64, 255, 256, w.Nq // 2, w.Nq - 65, w.Nq - 2, w.Nq - 1]
+    rows = {(p // w.H, p % w.H, i) for p in bh for i in edges if 0 <= i < w.Nq}
+    for b in range(w.B):
+        rows |= {(b, int(rng.integers(w.H)), i) for i in (0, w.Nq - 1)}
+    rows |= {(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.Nq)))
+             for _ in range(48)}
+    return sorted(rows)
+
+
+def oracle_reference_rows(w, q, k, v, lens, rows):
+    """The fp64 oracle's O and LSE on the check rows (the oracle leg of the bench)."""
+    import oracle
+    return oracle.attention_oracle_rows(q, k, v, w.scale, w.causal, lens, rows)
+
+
+O_TOL, LSE_RTOL = 2e-2, 1e-3   # bf16 inputs, fp32 accumulation, bf16 O; LSE floor 1
+
+
+def compare_rows(o_gpu, lse_gpu, o_ref, lse_ref):
+    """max |dO|, max LSE error (relative, floor 1) and -inf placement on the check rows."""
+    import numpy as np
+    inf_ref, inf_gpu = np.isneginf(lse_ref), np.isneginf(lse_gpu)
+    fin = ~inf_ref
+    err_o = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
+    err_l = float(np.max(np.abs(lse_gpu[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(
+        lse_ref[fin])))) if fin.any() else 0.0
+    placement = bool(np.array_equal(inf_ref, inf_gpu)) and bool(np.all(o_gpu[inf_ref] == 0.0))
+    return {"rows": int(len(lse_ref)), "empty_rows": int(inf_ref.sum()),
+            "max_abs_err_o": err_o, "max_lse_err": err_l, "empty_rows_exact": placement,
+            "tol_o": O_TOL, "tol_lse": LSE_RTOL,
+            "pass": bool(err_o <= O_TOL and err_l <= LSE_RTOL and placement)}
 
 
 SOFTMAX_ROWS, SOFTMAX_COLS, SOFTMAX_SEED = 8192, 8192, 6
@@ -388,6 +490,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--clock-trace", default=None,
+                    help="write the shader-clock samples (JSON) to this path")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="calls timed with a 512 MiB buffer written before each (0: skip)")
     ap.add_argument("--op", choices=["attention", "partial", "materialized", "softmax_rows",
@@ -413,21 +517,33 @@ def main():
                 "fp8": bench_fp8}[args.op](args)
 
     import numpy as np
-    import torch
 
-    from exact_attention_89_amd import api
     from exact_attention_89_amd.workloads import HEADLINE, WORKLOADS, generate
 
-    if not os.path.exists(api.library_path()):
-        from exact_attention_89_amd import build
-        build.build()
-    api.load_library()
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
     if w.dtype != "bf16":
         raise SystemExit("bench.py times the bf16 path")
     log(f"[bench] generating {name}")
     q, k, v, lens = generate(w)
+
+    # The oracle leg runs before this process touches the GPU (its pool forks): the
+    # reference rows for the parity check, then the timed CPU baseline.
+    rows = check_rows(w)
+    log(f"[bench] oracle on {len(rows)} check rows")
+    o_ref, lse_ref = oracle_reference_rows(w, q, k, v, lens, rows)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu_baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline_attention(w, q, k, v, lens, args.cpu_seconds)
+
+    import torch
+
+    from exact_attention_89_amd import api
+    if not os.path.exists(api.library_path()):
+        from exact_attention_89_amd import build
+        build.build()
+    api.load_library()
     dev = torch.device("cuda:0")
     qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
     ld = None if lens is None else torch.from_numpy(lens).to(dev)
@@ -457,20 +573,25 @@ def main():
         # S fp32 written once and read twice, P bf16 written once and read once
         extra_bytes = (4 + 8 + 2 + 2) * w.B * w.H * w.Nq * ldk
 
+    stream = torch.cuda.current_stream()
+    clock = ClockProbe(api, torch, dev, w, args)
     log(f"[bench] warmup {args.warmup}")
+    clock.begin(1)
     for _ in range(args.warmup):
         step()
+    clock.end(1, stream)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    clock.begin(2)
     for s, e in ev:
         s.record(stream)
         step()
         e.record(stream)
+    clock.end(2, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in ev]
@@ -483,7 +604,19 @@ def main():
     log(f"[bench] {name}: {ms_per_step:.4f} ms/step (events), wall {wall / args.steps * 1e3:.4f}"
         f" ms/step, launch median {np.median(launch_ms):.4f} ms, p10 "
         f"{np.percentile(launch_ms, 10):.4f}, p90 {np.percentile(launch_ms, 90):.4f}")
-    assert not torch.isnan(o).any().item(), "NaN in the output"
+
+    # parity of what was timed: the check rows against the oracle, NaNs over everything
+    nan_count = int(torch.isnan(o).sum().item()) + int(torch.isnan(lse).sum().item())
+    idx = tuple(torch.tensor(c, dtype=torch.long, device=dev) for c in zip(*rows))
+    o_rows = o[idx].float().cpu().numpy().astype(np.float64)
+    lse_rows = lse[idx].cpu().numpy().astype(np.float64)
+    check = compare_rows(o_rows, lse_rows, o_ref, lse_ref)
+    check["nan_count"] = nan_count
+    check["pass"] = bool(check["pass"] and nan_count == 0)
+    log(f"[bench] check vs oracle on {check['rows']} rows: max|dO| {check['max_abs_err_o']:.3e}, "
+        f"LSE err {check['max_lse_err']:.3e}, NaN {nan_count}, "
+        f"{'pass' if check['pass'] else 'FAIL'}")
+
     launch_stats = {"median": round(float(np.median(launch_ms)), 5),
                     "p10": round(float(np.percentile(launch_ms, 10)), 5),
                     "p90": round(float(np.percentile(launch_ms, 90)), 5)}
@@ -494,11 +627,13 @@ def main():
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.cold_steps)]
+        clock.begin(3)
         for s_, e in cev:
             scratch.fill_(1)
             s_.record(stream)
             step()
             e.record(stream)
+        clock.end(3, stream)
         torch.cuda.synchronize()
         cold_ms = [s_.elapsed_time(e) for s_, e in cev]
         cold = {"median_ms": round(float(np.median(cold_ms)), 5),
@@ -507,11 +642,11 @@ def main():
                 "calls": args.cold_steps}
         del scratch
         log(f"[bench] cold (512 MiB written between calls): median {cold['median_ms']:.4f} ms")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log(f"[bench] cpu_baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
-        cpu = cpu_baseline(w, q, k, v, lens, args.cpu_seconds)
+    clocks = clock.finish()
+    if clocks:
+        log(f"[bench] shader clock: timed region {clocks.get('timed_mhz')} MHz (1 ms windows "
+            f"{clocks.get('timed_1ms_min_mhz')}-{clocks.get('timed_1ms_max_mhz')}), warm-up "
+            f"{clocks.get('warmup_mhz')} MHz, cold calls {clocks.get('cold_mhz')} MHz")
 
     if args.op != "attention":
         # multi-launch paths: bound by device memory; bytes = inputs + outputs + the
@@ -528,15 +663,31 @@ def main():
             "data": "synthetic",
             "config": {"workload": name, "op": args.op, "B": w.B, "H": w.H, "Nq": w.Nq,
                        "Nk": w.Nk, "D": w.D, "causal": w.causal, "seed": w.seed,
-                       "algorithmic_bytes_per_call": algo_bytes},
+                       "algorithmic_bytes_per_call": algo_bytes, "check": check,
+                       "clock": clocks},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
             "cpu_baseline": cpu,
         }
         print(json.dumps(line), flush=True)
-        return
+        sys.exit(0 if check["pass"] else 1)
 
     traffic = measured_traffic(name)
+    config = {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
+              "causal": w.causal, "seed": w.seed,
+              "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+              "launch_ms": launch_stats, "cold": cold, "clock": clocks, "check": check,
+              "versions": versions(torch)}
+    if lens is not None:
+        # key padding: the metric counts every key slot; the work that exists is the
+        # valid keys, 4*H*Nq*D*sum(kv_len) (halved when causal)
+        eff = effective_flops(w, lens)
+        config["kv_lens"] = [int(x) for x in lens]
+        config["valid_key_fraction"] = round(float(eff / flops), 4)
+        config["effective_flops"] = eff
+        config["effective_tflops"] = round(eff / (ms_per_step * 1e-3) / 1e12, 2)
+        config["effective_frac"] = round(eff / (mean_launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                         4)
     line = {
         "metric": "fused attn fwd TFLOP/s + % bf16 MFMA peak (B,H,N,D=1,32,8192,128 causal)",
         "value": round(value, 2),
@@ -550,16 +701,110 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
-                   "causal": w.causal, "seed": w.seed,
-                   "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-                   "launch_ms": launch_stats, "cold": cold, "versions": versions(torch)},
+        "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if not check["pass"]:
+        log("[bench] the timed output does not match the oracle")
+        sys.exit(1)
+
+
+def effective_flops(w, lens):
+    """4*H*Nq*D*sum(clamped kv_len), halved when causal: the work over valid keys only."""
+    tot = sum(min(max(int(x), 0), w.Nk) for x in lens)
+    f = 4.0 * w.H * w.Nq * w.D * tot
+    return f / 2.0 if w.causal else f
+
+
+class ClockProbe:
+    """The shader clock while bench.py runs.  For each segment of the run (1 warm-up, 2 the
+    timed region, 3 the cold calls) one sampling wave on a stream of its own records its
+    shader-cycle and wall-tick counters every few tens of microseconds; a mark enqueued on
+    the launch stream behind the segment's last call ends it.  The clock of a segment is
+    the ratio of the two counters' increments between its first and last sample."""
+
+    MAX_SAMPLES = 4096
+    NAMES = {1: "warmup", 2: "timed", 3: "cold"}
+
+    def __init__(self, api, torch, dev, w, args):
+        self.api, self.torch = api, torch
+        self.hz = api.clock_wall_hz()
+        est_step = w.metric_flops() / 3e14 + 50e-6        # a generous 300 TFLOP/s + launch
+        if args.op != "attention":
+            est_step *= 10.0                                # the multi-launch paths
+        # upper bounds only: each segment's sampler normally ends at its mark
+        self.calls = {1: args.warmup, 2: args.steps, 3: args.cold_steps}
+        self.est = {i: 1.5 * n * (est_step + (2e-4 if i == 3 else 0.0)) + 0.2
+                    for i, n in self.calls.items()}
+        self.buf = {i: torch.zeros(3 * self.MAX_SAMPLES + 1, dtype=torch.int64, device=dev)
+                    for i in self.calls}
+        self.phase = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.side = torch.cuda.Stream(device=dev)
+        self.interval = {}
+        self.trace_path = getattr(args, "clock_trace", None)
+        torch.cuda.synchronize()
+
+    def begin(self, seg):
+        dur = min(30.0, self.est[seg])
+        self.interval[seg] = max(int(self.hz * 2e-5),
+                                 int(self.hz * dur / (self.MAX_SAMPLES - 1)) + 1)
+        self.api.clock_sampler(self.buf[seg], self.phase, seg, self.MAX_SAMPLES,
+                               self.interval[seg], int(dur * self.hz), stream=self.side)
+
+    def end(self, seg, stream):
+        self.api.clock_mark(self.phase, seg, stream=stream)
+
+    def _segment(self, seg):
+        import numpy as np
+        if seg not in self.interval:
+            return None
+        raw = self.buf[seg].cpu().numpy()
+        n = int(raw[0])
+        if n < 2:
+            return None
+        tri = raw[1:1 + 3 * n].reshape(n, 3).astype(np.float64)
+        return tri[:, 0], tri[:, 1]
+
+    def _mhz(self, rt, ct):
+        if len(rt) < 2 or rt[-1] <= rt[0]:
+            return None
+        return round(float((ct[-1] - ct[0]) / (rt[-1] - rt[0]) * self.hz / 1e6), 1)
+
+    def finish(self):
+        import numpy as np
+        self.side.synchronize()
+        self.torch.cuda.synchronize()
+        out, trace = {}, {"hz": self.hz}
+        for seg, name in self.NAMES.items():
+            r = self._segment(seg)
+            if r is None:
+                out[f"{name}_mhz"] = None
+                continue
+            rt, ct = r
+            out[f"{name}_mhz"] = self._mhz(rt, ct)
+            if seg == 2:
+                # 1 ms windows over the timed region: the spread within it
+                win = []
+                for lo in np.arange(rt[0], rt[-1], 1e-3 * self.hz):
+                    sel = (rt >= lo) & (rt <= lo + 1e-3 * self.hz)
+                    m = self._mhz(rt[sel], ct[sel])
+                    if m is not None:
+                        win.append(m)
+                out["timed_1ms_min_mhz"] = min(win) if win else None
+                out["timed_1ms_max_mhz"] = max(win) if win else None
+                out["timed_samples"] = int(len(rt))
+                out["timed_span_ms"] = round(float((rt[-1] - rt[0]) / self.hz * 1e3), 3)
+            trace[name] = {"rt": (rt - rt[0]).tolist(), "ct": (ct - ct[0]).tolist()}
+        if self.trace_path:
+            with open(self.trace_path, "w") as f:
+                json.dump(trace, f)
+        out["method"] = ("s_memtime / s_memrealtime increments on one sampling wave running "
+                         "beside each segment")
+        return out
 
 
 if __name__ == "__main__":

@@ -34,6 +34,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
+_U64 = ctypes.c_uint64
 EXPORTS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
     "attn_fwd_select_kernel": (_I, [_I]),
@@ -55,6 +56,9 @@ EXPORTS = {
     "softmax_rows_f32": (_I, [_P, _P, _I, _I, _P]),
     "softmax_rows_unfused_workspace_bytes": (_SZ, [_I]),
     "softmax_rows_unfused_f32": (_I, [_P, _P, _I, _I, _P, _SZ, _P]),
+    "attn_clock_sampler": (_I, [_P, _P, _I, _I, _U64, _U64, _P]),
+    "attn_clock_mark": (_I, [_P, _I, _P]),
+    "attn_clock_wall_hz": (ctypes.c_int64, []),
 }
 
 
@@ -365,3 +369,39 @@ def attn_fwd_splitkv(q, k, v, scale: Optional[float] = None, causal: bool = Fals
 def torch_bf16():
     import torch
     return torch.bfloat16
+
+
+# ---- shader-clock sampling (include/gpu_clock.h), a measurement aid ----
+
+def clock_wall_hz() -> int:
+    """Frequency of the device's wall-clock counter in Hz."""
+    hz = int(load_library().attn_clock_wall_hz())
+    if hz <= 0:
+        raise AttnError(hz, "attn_clock_wall_hz")
+    return hz
+
+
+def clock_sampler(samples, phase, stop_value: int, max_samples: int, interval_ticks: int,
+                  duration_ticks: int, stream=None) -> None:
+    """Start the one-wave sampler writing (wall ticks, shader cycles, phase) triples into
+    ``samples`` (int64 GPU tensor of 3 * max_samples + 1 entries; ``phase`` an int32 GPU
+    tensor) on ``stream``; it ends once ``phase`` holds ``stop_value``."""
+    import torch
+    if samples.dtype != torch.int64 or samples.numel() < 3 * max_samples + 1:
+        raise ValueError("samples must be an int64 tensor of 3 * max_samples + 1 entries")
+    if phase.dtype != torch.int32 or phase.numel() < 1:
+        raise ValueError("phase must be an int32 tensor")
+    s = (stream or torch.cuda.current_stream(samples.device)).cuda_stream
+    _check(load_library().attn_clock_sampler(samples.data_ptr(), phase.data_ptr(),
+                                             int(stop_value), int(max_samples),
+                                             int(interval_ticks), int(duration_ticks), s),
+           "attn_clock_sampler")
+
+
+def clock_mark(phase, value: int, stream=None) -> None:
+    """Store ``value`` into ``phase`` (int32 GPU tensor) when ``stream`` reaches this point."""
+    import torch
+    if phase.dtype != torch.int32 or phase.numel() < 1:
+        raise ValueError("phase must be an int32 tensor")
+    s = (stream or torch.cuda.current_stream(phase.device)).cuda_stream
+    _check(load_library().attn_clock_mark(phase.data_ptr(), int(value), s), "attn_clock_mark")

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
                             "softmax_rows_unfused_f32", "attn_partial",
                             "attn_partial_workspace_bytes", "attn_fwd_splitkv",
                             "attn_splitkv_num_splits", "attn_splitkv_workspace_bytes",
-                            "attn_fwd_fp8", "attn_fwd_varlen"])
+                            "attn_fwd_fp8", "attn_fwd_varlen", "attn_clock_sampler",
+                            "attn_clock_mark", "attn_clock_wall_hz"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -164,7 +165,7 @@ def test_splitkv_plan_and_checks(lib):
 
 
 def test_headers_compile_and_link_as_c(tmp_path, lib):
-    """A C99 program (gcc, -Wall -Wextra -pedantic -Werror) includes both headers,
+    """A C99 program (gcc, -Wall -Wextra -pedantic -Werror) includes every header,
     takes the address of every declared function (so the linker resolves each one
     against libattn89.so) and calls the host-side checks: the boundary is plain C."""
     import shutil
@@ -175,7 +176,8 @@ def test_headers_compile_and_link_as_c(tmp_path, lib):
     names = _declared()
     src = tmp_path / "abi.c"
     src.write_text(
-        "#include <stdio.h>\n#include \"attn.h\"\n#include \"softmax_rows.h\"\n"
+        "#include <stdio.h>\n" +
+        "".join(f"#include \"{os.path.basename(h)}\"\n" for h in HEADERS) +
         "typedef void (*fn_t)(void);\n"
         "static const fn_t all[] = {" + ", ".join(f"(fn_t){n}" for n in names) + "};\n"
         "int main(void) {\n"
