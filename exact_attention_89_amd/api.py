@@ -21,7 +21,7 @@ ATTN_OK = 0
 _STATUS_NAMES = {
     -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
     -4: "ATTN_ERR_ALIGN", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_WORKSPACE",
-    -7: "ATTN_ERR_HIP", -8: "ATTN_ERR_TOO_LARGE",
+    -7: "ATTN_ERR_HIP", -8: "ATTN_ERR_TOO_LARGE", -9: "ATTN_ERR_SCRATCH",
 }
 
 # bf16 forward kernel choice (attn_fwd_select_kernel)
@@ -51,6 +51,8 @@ EXPORTS = {
     "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _P, _SZ,
                               _P]),
     "attn_partial": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _SZ, _P]),
+    "attn_fwd_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I,
+                                      _P]),
     "attn_strerror": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
     "softmax_rows_f32": (_I, [_P, _P, _I, _I, _P]),
@@ -363,6 +365,27 @@ def attn_fwd_splitkv(q, k, v, scale: Optional[float] = None, causal: bool = Fals
                               workspace.numel() * workspace.element_size(),
                               _stream_handle(torch, q.device))
     _check(st, "attn_fwd_splitkv")
+    return o, l
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, scale: Optional[float] = None, causal: bool = False,
+                             kv_lens=None, num_splits: int = 0, out=None, lse=None):
+    """attn_fwd_splitkv with the library's fixed scratch instead of a workspace (the
+    C entry point allocates nothing; pass ``out`` and ``lse`` to allocate nothing here
+    either)."""
+    torch, q, k, v, kv_lens, (B, H, Nq, Nk, D) = _prep(q, k, v, kv_lens, torch_bf16())
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = load_library().attn_fwd_splitkv_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Nq, Nk, D,
+        float(scale), int(bool(causal)), kv_lens.data_ptr() if kv_lens is not None else None,
+        int(num_splits), _stream_handle(torch, q.device))
+    _check(st, "attn_fwd_splitkv_noalloc")
     return o, l
 
 

@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -221,10 +223,17 @@ size_t attn_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int D, int num
   return total;
 }
 
-int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int H, int Nq, int Nk, int D, float scale, int causal,
-                     const int32_t* kv_lens, int num_splits, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks and the launch of attn_fwd_splitkv and attn_fwd_splitkv_noalloc.  When
+// `need` is not null the workspace is not checked: the caller learns the bytes the
+// problem needs through it and passes its own buffer afterwards.
+int splitkv_checked(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int Nq, int Nk, int D, float scale, int causal,
+                    const int32_t* kv_lens, int num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream, size_t* need) {
   int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, kv_lens, 2);
   if (st != ATTN_OK) return st;
   if (((size_t)Nq + 256) * D * 2 >= ((size_t)1 << 31) ||
@@ -235,6 +244,10 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   if (!splitkv_layout(B, H, Nq, Nk, D, num_splits, &splits, &chunk, &lse_off, &total))
     return ATTN_ERR_SHAPE;
   if ((long long)((Nq + 127) / 128) * B * H * splits > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  if (need) {
+    *need = total;
+    return ATTN_OK;
+  }
   if (!workspace || workspace_bytes < total || !aligned(workspace, 256))
     return ATTN_ERR_WORKSPACE;
   attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
@@ -243,6 +256,63 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   a.o_part = (float*)workspace;
   a.lse_part = (float*)((char*)workspace + lse_off);
   return attn89::launch_attn_splitkv(a, D, (hipStream_t)stream);
+}
+
+// The fixed scratch of attn_fwd_splitkv_noalloc: one copy per device, held from the
+// library's load until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, looked up once per device (with that device current) and kept.
+constexpr size_t kScratchBytes = (size_t)ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or null (status in *st).
+void* scratch_address(int* st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *st = ATTN_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *st = ATTN_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *st = ATTN_OK;
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Nq, int Nk, int D, float scale, int causal,
+                     const int32_t* kv_lens, int num_splits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return splitkv_checked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, kv_lens, num_splits,
+                         workspace, workspace_bytes, stream, nullptr);
+}
+
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                             const int32_t* kv_lens, int num_splits, void* stream) {
+  size_t need = 0;
+  int st = splitkv_checked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, kv_lens,
+                           num_splits, nullptr, 0, stream, &need);
+  if (st != ATTN_OK) return st;
+  if (need > kScratchBytes) return ATTN_ERR_SCRATCH;
+  void* ws = scratch_address(&st);
+  if (!ws) return st;
+  return splitkv_checked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, kv_lens, num_splits,
+                         ws, kScratchBytes, stream, nullptr);
 }
 
 size_t attn_partial_workspace_bytes(int B, int H, int Nq, int Nk) {
@@ -283,6 +353,8 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case ATTN_ERR_HIP: return "the HIP runtime reported a launch error";
     case ATTN_ERR_TOO_LARGE: return "problem exceeds the kernel launch limits";
+    case ATTN_ERR_SCRATCH:
+      return "problem needs more than the fixed scratch of attn_fwd_splitkv_noalloc";
     default: return "unknown status";
   }
 }

@@ -54,6 +54,7 @@ extern "C" {
 #define ATTN_ERR_WORKSPACE   -6  /* workspace NULL or smaller than required            */
 #define ATTN_ERR_HIP         -7  /* the HIP runtime reported an error at launch        */
 #define ATTN_ERR_TOO_LARGE   -8  /* grid would exceed the launch limits                */
+#define ATTN_ERR_SCRATCH     -9  /* more scratch than attn_fwd_splitkv_noalloc holds   */
 
 /*
  * attn_fwd -- the fused forward, bfloat16 inputs and output.
@@ -246,6 +247,29 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      int B, int H, int Nq, int Nk, int D, float scale, int causal,
                      const int32_t* kv_lens, int num_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The partial results live in a fixed scratch array of the library
+ * (ATTN_NOALLOC_SCRATCH_BYTES per device, allocated when the library is loaded
+ * and held until the process ends); the caller still owns q, k, v, o, lse and
+ * kv_lens.  Same arguments (minus workspace), semantics, kernels and results as
+ * attn_fwd_splitkv with the same num_splits.
+ *
+ * Errors: every status of attn_fwd_splitkv except ATTN_ERR_WORKSPACE, plus
+ * ATTN_ERR_SCRATCH when attn_splitkv_workspace_bytes(B, H, Nq, Nk, D, num_splits)
+ * exceeds ATTN_NOALLOC_SCRATCH_BYTES (nothing is launched); ATTN_ERR_HIP if the
+ * scratch address cannot be obtained.  Nothing in the scratch must start at zero
+ * (every partial result is written before it is read).  All calls on one device
+ * share its scratch: calls that may overlap on that device (different streams,
+ * or other threads) race and must be ordered by the caller.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                             const int32_t* kv_lens, int num_splits, void* stream);
 
 /* attn_strerror -- a static, NUL-terminated description of a status code. */
 const char* attn_strerror(int status);

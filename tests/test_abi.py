@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
                             "softmax_rows_unfused_f32", "attn_partial",
                             "attn_partial_workspace_bytes", "attn_fwd_splitkv",
                             "attn_splitkv_num_splits", "attn_splitkv_workspace_bytes",
-                            "attn_fwd_fp8", "attn_fwd_varlen", "attn_clock_sampler",
+                            "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv_noalloc",
+                            "attn_clock_sampler",
                             "attn_clock_mark", "attn_clock_wall_hz"])
 
 
@@ -50,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     assert lib.attn_abi_version() == 2
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert lib.attn_strerror(st)
     assert lib.attn_strerror(-99) == b"unknown status"
 
@@ -196,3 +197,24 @@ def test_headers_compile_and_link_as_c(tmp_path, lib):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.split() == ["2", "-1", "-1", str(len(names))]
+
+
+def test_splitkv_noalloc_host_checks(lib):
+    """attn_fwd_splitkv_noalloc: argument checks and the fixed-scratch limit are host
+    checks, decided before the scratch address is looked up or anything is launched."""
+    p = ctypes.c_void_p(0x10000)
+    limit = 16 << 20                                   # ATTN_NOALLOC_SCRATCH_BYTES
+    assert api.NOALLOC_SCRATCH_BYTES == limit
+    big = (1, 64, 4096, 65536, 128, 64)                # B, H, Nq, Nk, D, splits
+    assert lib.attn_splitkv_workspace_bytes(*big) > limit
+
+    def call(q=p, B=1, H=64, Nq=4096, Nk=65536, D=128, splits=64, scale=0.1):
+        return lib.attn_fwd_splitkv_noalloc(q, p, p, p, p, B, H, Nq, Nk, D,
+                                            ctypes.c_float(scale), 0, None, splits, None)
+
+    assert call() == -9                                # does not fit the scratch
+    assert lib.attn_strerror(-9)
+    assert call(q=None) == -1
+    assert call(D=96) == -3
+    assert call(B=0) == -2
+    assert call(scale=float("nan")) == -5
