@@ -74,7 +74,9 @@ class AttnError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree HIP library, or the build named by ATTN89_LIBRARY (used by the tests
+    to load a host-sanitised build of the same sources)."""
+    return os.environ.get("ATTN89_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 
 def load_library(path: Optional[str] = None):

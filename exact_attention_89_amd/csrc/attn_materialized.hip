@@ -44,7 +44,8 @@ __global__ __launch_bounds__(256) void qk_scores_kernel(FwdArgs p, float scale, 
   for (int s = 0; s < D / 16; ++s) {
     bf16x8 a = {}, bb = {};
     if (qi < p.Nq) a = *(const bf16x8*)(qp + (size_t)qi * D + 16 * s + 8 * lg);
-    if (kj < p.Nk) bb = *(const bf16x8*)(kp + (size_t)kj * D + 16 * s + 8 * lg);
+    // keys past the sequence's length are never read (their scores are masked anyway)
+    if (kj < L) bb = *(const bf16x8*)(kp + (size_t)kj * D + 16 * s + 8 * lg);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
   }
   // accumulator register r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32
@@ -128,13 +129,17 @@ __global__ __launch_bounds__(256) void pv_kernel(FwdArgs p, int ld, const unsign
   const unsigned short* vp = (const unsigned short*)p.v + (size_t)bh * p.Nk * D;
   const unsigned short* ph = P + (size_t)bh * p.Nq * ld;
   unsigned short* op = (unsigned short*)p.o + (size_t)bh * p.Nq * D;
+  // V rows past the sequence's key length are never read: their probabilities are 0,
+  // but a NaN or Inf there would still turn 0 * x into NaN in the product
+  const int L = clamp_len(p.kv_lens, bh / p.H, p.Nk);
+  const int j_end = (L + BC - 1) / BC * BC;
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) acc[d] = (f32x16){};
   const int qi = i0 + lq;
 
-  for (int j0 = 0; j0 < ld; j0 += BC) {
+  for (int j0 = 0; j0 < j_end; j0 += BC) {
     __syncthreads();
     for (int u = tid; u < (BC / 4) * (D / 8); u += 256) {
       const int kg = u % (BC / 4), dg = u / (BC / 4);
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(256) void pv_kernel(FwdArgs p, int ld, const unsign
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = j0 + 4 * kg + r;
-        vr[r] = key < p.Nk ? *(const u32x4*)(vp + (size_t)key * D + 8 * dg) : (u32x4){0, 0, 0, 0};
+        vr[r] = key < L ? *(const u32x4*)(vp + (size_t)key * D + 8 * dg) : (u32x4){0, 0, 0, 0};
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {

@@ -1,11 +1,12 @@
 // attn_partial.hip -- partial fusion: Q K^T and the softmax in one launch, the
 // probabilities written to device memory, P V in a second launch.
 //
-// Page "Attention softmax fusion", section "What fused has to mean": fusing the
-// softmax into the QK stage keeps the score tile in registers from the contraction
-// through the row maximum, the exponential and the division, but the probabilities
-// still leave the chip because a separate P V has to read them; one boundary fused
-// removes half of the score-sized traffic and leaves an Nq x Nk tensor behind.
+// Page "Attention softmax fusion", section "What fused has to mean" (the case where
+// only one of the two boundaries is fused): each score tile stays on chip from the
+// Q K^T contraction until it is a normalised probability, yet P is still stored,
+// since the P V launch is separate and can only get it from device memory.  About
+// half of the score-sized traffic of the three-launch form remains, and an Nq x Nk
+// tensor is still materialised.
 //
 // Launch 1 (this file), one workgroup = 4 waves = 128 query rows:
 //   pass 1  for every key tile: S = K Q^T (MFMA, fp32), mask, and the online row

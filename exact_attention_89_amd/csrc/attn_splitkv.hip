@@ -8,8 +8,8 @@
 // the attention of its queries over its key range only, normalised by its own sum:
 // O_s and LSE_s = log sum over its keys of exp(score).  The rows of the full
 // softmax follow from the same rescaling the online recurrence uses (page "Attention
-// softmax fusion", section "The tile loop": multiply by exp(m_old - m_new) before
-// adding a new part), applied to whole ranges:
+// softmax fusion", section "The tile loop": the sums kept so far are scaled by
+// exp(m_old - m_new) when a new part raises the maximum), applied to whole ranges:
 //
 //   LSE = log sum_s exp(LSE_s)            (computed against the largest LSE_s)
 //   O   = sum_s exp(LSE_s - LSE) O_s

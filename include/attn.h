@@ -199,12 +199,12 @@ int attn_materialized(const void* q, const void* k, const void* v, void* o, floa
 size_t attn_partial_workspace_bytes(int B, int H, int Nq, int Nk);
 
 /*
- * attn_partial -- partial fusion, two launches: Q.K^T and the softmax fused in
- * one kernel that keeps each score tile in registers through the row maximum,
- * the exponential and the division, but writes the probabilities P (bfloat16)
- * to the workspace; then O = P V in a second kernel that reads them back (page
- * "Attention softmax fusion", section "What fused has to mean": fusing one
- * boundary leaves a score-sized tensor behind).  The first kernel visits the
+ * attn_partial -- partial fusion, two launches.  The first kernel fuses Q.K^T
+ * with the softmax (a score tile is normalised without leaving the chip) and
+ * stores the probabilities P (bfloat16) in the workspace; the second computes
+ * O = P V from them (page "Attention softmax fusion", section "What fused has
+ * to mean": with only that boundary fused, a score-sized tensor still goes
+ * through device memory).  The first kernel visits the
  * key tiles twice (row statistics, then P), so it spends twice the Q.K^T
  * arithmetic of attn_fwd; masked entries and key tiles no query of a block can
  * see are written as zeros, so every column below ld is defined.

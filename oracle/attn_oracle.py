@@ -30,14 +30,14 @@ Two functions compute this:
 
 * ``attention_oracle`` is the plain definition: it materialises the whole score
   row, masks it, and applies the stable softmax and the value contraction.
-* ``attention_online_oracle`` follows the online recurrence that the pages give
-  (page "Attention softmax fusion", section "The tile loop"; page "Kernel
-  Fusion and the Memory Wall", sections "FlashAttention: avoid the full score
-  matrix" and "A small executable reference"): keys are visited tile by tile,
-  a running maximum m, normaliser l and unnormalised numerator a are kept, and
-  on every tile the old accumulators are multiplied by exp(m - m').  After the
-  last tile the result is a / l.  It exists so that tests can show the
-  recurrence reaches the same result as the definition.
+* ``attention_online_oracle`` is the online recurrence the pages describe (page
+  "Attention softmax fusion", section "The tile loop"; page "Kernel Fusion and
+  the Memory Wall", sections "FlashAttention: avoid the full score matrix" and
+  "A small executable reference"), restated block by block over all rows of a
+  head: a running maximum, a running sum of exponentials and a running weighted
+  sum of values, with the old sums rescaled by exp(old max - new max) whenever
+  the maximum moves, and one division at the end.  It exists so that tests can
+  show the recurrence reaches the same result as the definition.
 
 Readings where the pages are silent (each one is listed in the design notes):
 
@@ -58,8 +58,6 @@ Every input is upcast to float64 before any arithmetic.
 """
 
 from __future__ import annotations
-
-import math
 
 import numpy as np
 
@@ -172,24 +170,28 @@ def attention_oracle(q, k, v, scale: float, causal: bool = False, kv_lens=None,
 
 def attention_online_oracle(q, k, v, scale: float, causal: bool = False, kv_lens=None,
                             tile: int = 64):
-    """The online (tile-by-tile) recurrence, in float64, one query row at a time.
+    """The online (block-by-block) form of the same function, in float64.
 
-    For each query row, keys are visited in tiles of ``tile``.  With the running
-    maximum m, normaliser l and numerator a of the keys seen so far, and the
-    scores s_t of the next tile:
+    For each (b, h) the keys are cut into consecutive blocks of ``tile`` and visited in
+    order; all query rows of the head advance together.  Per row, three running values
+    summarise the keys seen so far:
 
-        m'   = max(m, max s_t)
-        c    = exp(m - m')            (the correction of the old accumulators)
-        l    = c * l + sum exp(s_t - m')
-        a    = c * a + exp(s_t - m') @ v_t
-        m    = m'
+        top   the largest masked score so far (-inf while none is valid),
+        den   the sum of exp(score - ref) over them,
+        num   the sum of exp(score - ref) * v_j over them (a row vector),
 
-    and after the last tile O = a / l, LSE = m + ln l.  Masked scores are -inf.
-    While every score seen is -inf, m and m' are -inf; the exponent references
-    are then taken as 0 (the guard), so c = exp(-inf) = 0 and no NaN appears.
-    A row whose l is 0 at the end has no valid key: O = 0, LSE = -inf.
+    where the exponent reference ``ref`` is ``top``, or 0 while ``top`` is -inf (the
+    guard: the reference never takes the value -inf, so -inf - (-inf) never occurs).
+    A new block raises ``top`` to ``max(top, block row max)``; the sums kept so far
+    were taken against the old reference, so both are first multiplied by
+    exp(old ref - new ref), the correction the pages apply whenever the maximum moves
+    (0 for rows that had no valid key yet, whose sums are empty); then the block's
+    weights exp(score - new ref), exactly 0 at masked keys, are added.  After the last
+    block, a row with den > 0 gets O = num / den and LSE = top + ln(den); a row with
+    den = 0 has no valid key: O = 0, LSE = -inf.
 
-    Slow (pure-Python loop over rows): for small shapes only.
+    It exists so that tests can show this recurrence reaches the definition's result
+    for every block size.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -201,28 +203,26 @@ def attention_online_oracle(q, k, v, scale: float, causal: bool = False, kv_lens
     o = np.zeros((B, H, Nq, Dv))
     lse = np.full((B, H, Nq), -np.inf)
     for b in range(B):
-        L = kv_length(kv_lens, b, Nk)
+        allowed = valid_keys(0, Nq, Nk, causal, kv_length(kv_lens, b, Nk))
         for h in range(H):
-            valid_all = valid_keys(0, Nq, Nk, causal, L)
-            for i in range(Nq):
-                scores = sigma * (k[b, h] @ q[b, h, i])
-                scores = np.where(valid_all[i], scores, -np.inf)
-                maximum = -np.inf
-                normalizer = 0.0
-                numerator = np.zeros(Dv)
-                for start in range(0, Nk, tile):
-                    s_t = scores[start:start + tile]
-                    new_maximum = max(maximum, float(s_t.max()))
-                    ref_new = 0.0 if new_maximum == -np.inf else new_maximum
-                    ref_old = 0.0 if maximum == -np.inf else maximum
-                    correction = math.exp(ref_old - ref_new) if maximum > -np.inf else 0.0
-                    tile_exp = np.exp(s_t - ref_new)
-                    normalizer = correction * normalizer + tile_exp.sum()
-                    numerator = correction * numerator + tile_exp @ v[b, h, start:start + tile]
-                    maximum = new_maximum
-                if normalizer > 0.0:
-                    o[b, h, i] = numerator / normalizer
-                    lse[b, h, i] = maximum + math.log(normalizer)
+            scores = np.where(allowed, sigma * (q[b, h] @ k[b, h].T), -np.inf)
+            top = np.full(Nq, -np.inf)
+            den = np.zeros(Nq)
+            num = np.zeros((Nq, Dv))
+            for lo in range(0, Nk, tile):
+                blk = scores[:, lo:lo + tile]
+                seen = top > -np.inf
+                raised = np.maximum(top, blk.max(axis=1))
+                ref_old = np.where(seen, top, 0.0)
+                ref_new = np.where(raised > -np.inf, raised, 0.0)
+                keep = np.exp(np.where(seen, ref_old - ref_new, -np.inf))
+                weights = np.exp(blk - ref_new[:, None])
+                den = keep * den + weights.sum(axis=1)
+                num = keep[:, None] * num + weights @ v[b, h, lo:lo + tile]
+                top = raised
+            has_key = den > 0.0
+            o[b, h, has_key] = num[has_key] / den[has_key, None]
+            lse[b, h, has_key] = top[has_key] + np.log(den[has_key])
     return o, lse
 
 

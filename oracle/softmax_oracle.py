@@ -23,9 +23,9 @@ one the attention oracle uses for a query with no valid key.
 Two functions compute this:
 
 * ``softmax_rows`` is the plain definition above.
-* ``softmax_rows_four_pass`` takes the unfused steps in the order the page lists
-  them: read the row for its maximum, read it again to write the exponentials,
-  read those for their sum, read them again to write the normalised output.  It
+* ``softmax_rows_four_pass`` takes the unfused steps in the page's order: a pass
+  over the row for its maximum, a pass that stores the exponentials, a pass that
+  sums them, and a pass that divides them by the sum.  It
   exists so tests can show that the step order gives the same function (the HIP
   unfused baseline follows the same four steps).
 

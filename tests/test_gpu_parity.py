@@ -109,7 +109,7 @@ def test_fused_bf16_kv_lens(lens, causal, D, bf16_kernel):
 
 def test_fused_bf16_beyond_4096_keys(bf16_kernel):
     """More than 4096 keys per row (page 'Attention softmax fusion', 'Things that
-    break': a stack allocation that dies at 4096 columns), odd length."""
+    break': a per-row buffer with a fixed 4096-column capacity), odd length."""
     _case("fused", 1, 2, 130, 4097, 128, False, seed=4097)
     _case("fused", 1, 1, 4099, 4099, 64, True, seed=4099)
 
@@ -223,6 +223,42 @@ def test_keys_beyond_kv_len_are_never_read(bf16_kernel):
         v2[b, :, L:] = float("nan")
     o2, l2 = api.attn_fwd(qd, k2, v2, kv_lens=ld)
     torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("path", ["partial", "materialized", "splitkv", "fp8"])
+def test_keys_beyond_kv_len_are_never_read_other_paths(path):
+    """The same for every other entry point that takes kv_lens: NaN keys and values at
+    or after kv_len leave the output bit for bit unchanged (and NaN-free)."""
+    q, k, v, _ = random_case(5, 2, 2, 200, 300, 64)
+    lens = np.array([0, 193], np.int32)
+    ld = _lens_dev(lens)
+    _say(f"[gpu] kv_len prefix, {path} path, 2x2x200x300 lens=[0,193]")
+    if path == "fp8":
+        qd, kd, vd = (torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.float8_e4m3fn)
+                      .view(torch.uint8) for x in (q, k, v))
+        nan = 0x7F                                     # an E4M3 NaN code
+    else:
+        qd, kd, vd = (_dev(x, "bf16") for x in (q, k, v))
+        nan = float("nan")
+
+    def run(kk, vv):
+        if path == "partial":
+            return api.attn_partial(qd, kk, vv, kv_lens=ld)
+        if path == "materialized":
+            return api.attn_materialized(qd, kk, vv, kv_lens=ld)
+        if path == "splitkv":
+            return api.attn_fwd_splitkv(qd, kk, vv, kv_lens=ld, num_splits=3)
+        return api.attn_fwd_fp8(qd, kk, vv, 0.02, 0.02, 0.02, kv_lens=ld)
+
+    o1, l1 = run(kd, vd)
+    k2, v2 = kd.clone(), vd.clone()
+    for b, L in enumerate(lens):
+        k2[b, :, L:] = nan
+        v2[b, :, L:] = nan
+    o2, l2 = run(k2, v2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o2.float()).any() and not torch.isnan(l2).any()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 

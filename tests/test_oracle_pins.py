@@ -542,20 +542,21 @@ def test_planted_online_mistakes_are_caught(monkeypatch):
     q, k, v = _rand(40, 1, 1, 6, 12, 4)
 
     def bad_online(q, k, v, scale, causal=False, kv_lens=None, tile=3):
+        # the online recurrence of the oracle with one change: the sums already kept
+        # are not rescaled when the running maximum rises
         q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
         sig = float(np.float32(scale))
-        o = np.zeros(q.shape[:3] + (v.shape[3],))
-        for i in range(q.shape[2]):
-            s = sig * (k[0, 0] @ q[0, 0, i])
-            m, l, a = -np.inf, 0.0, np.zeros(v.shape[3])
-            for st in range(0, s.size, tile):
-                mn = max(m, s[st:st + tile].max())
-                e = np.exp(s[st:st + tile] - mn)
-                l = l + e.sum()               # correction dropped
-                a = a + e @ v[0, 0, st:st + tile]
-                m = mn
-            o[0, 0, i] = a / l
-        return o
+        scores = sig * (q[0, 0] @ k[0, 0].T)
+        top = np.full(scores.shape[0], -np.inf)
+        den = np.zeros(scores.shape[0])
+        num = np.zeros((scores.shape[0], v.shape[3]))
+        for lo in range(0, scores.shape[1], tile):
+            blk = scores[:, lo:lo + tile]
+            top = np.maximum(top, blk.max(axis=1))
+            weights = np.exp(blk - top[:, None])
+            den = den + weights.sum(axis=1)
+            num = num + weights @ v[0, 0, lo:lo + tile]
+        return (num / den[:, None])[None, None]
     ref, _ = OA.attention_oracle(q, k, v, 0.8)
     assert not _close(bad_online(q, k, v, 0.8), ref, 1e-6)
     good, _ = OA.attention_online_oracle(q, k, v, 0.8, tile=3)
