@@ -28,6 +28,7 @@ _STATUS_NAMES = {
 ATTN_KERNEL_AUTO = 0
 ATTN_KERNEL_PINGPONG = 1
 ATTN_KERNEL_FOURWAVE = 2
+ATTN_KERNEL_KEYGROUPS = 3
 
 # exported symbol -> (restype, argtypes); must match include/attn.h
 _P = ctypes.c_void_p

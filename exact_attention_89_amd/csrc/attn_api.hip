@@ -84,12 +84,15 @@ int num_cus() {
 // The 8-wave ping-pong kernel (one 256-row workgroup per CU) is the faster one once
 // its blocks are full (Nq >= 256) and its grid covers every CU; below that, and for
 // D = 64 (where the softmax, not the matrix work, bounds a tile), the 4-wave kernel
-// with smaller blocks and twice as many workgroups wins.
+// with smaller blocks and twice as many workgroups wins.  When even its grid gives
+// no CU a second workgroup, the time is the longest block's key loop, and the key
+// groups variant halves that loop.
 int pick_bf16_kernel(int B, int H, int Nq, int D) {
   if (g_bf16_kernel != ATTN_KERNEL_AUTO) return g_bf16_kernel;
   const long long pp_grid = (long long)((Nq + 255) / 256) * B * H;
-  return (D == 128 && Nq >= 256 && pp_grid >= num_cus()) ? ATTN_KERNEL_PINGPONG
-                                                         : ATTN_KERNEL_FOURWAVE;
+  if (D == 128 && Nq >= 256 && pp_grid >= num_cus()) return ATTN_KERNEL_PINGPONG;
+  const long long grid4 = (long long)((Nq + 127) / 128) * B * H;
+  return grid4 <= num_cus() ? ATTN_KERNEL_KEYGROUPS : ATTN_KERNEL_FOURWAVE;
 }
 
 }  // namespace
@@ -107,9 +110,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
       ((size_t)Nk + 256) * D * 2 >= ((size_t)1 << 31))
     return ATTN_ERR_TOO_LARGE;
   attn89::FwdArgs a = make_args(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_lens);
-  if (pick_bf16_kernel(B, H, Nq, D) == ATTN_KERNEL_PINGPONG)
+  const int which = pick_bf16_kernel(B, H, Nq, D);
+  if (which == ATTN_KERNEL_PINGPONG)
     return attn89::launch_attn_fwd_bf16_pp(a, D, (hipStream_t)stream);
-  return attn89::launch_attn_fwd_bf16_4w(a, D, (hipStream_t)stream);
+  return attn89::launch_attn_fwd_bf16_4w(a, D, (hipStream_t)stream,
+                                         which == ATTN_KERNEL_KEYGROUPS ? 2 : 1);
 }
 
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -160,7 +165,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 
 int attn_fwd_select_kernel(int which) {
   if (which != ATTN_KERNEL_AUTO && which != ATTN_KERNEL_PINGPONG &&
-      which != ATTN_KERNEL_FOURWAVE)
+      which != ATTN_KERNEL_FOURWAVE && which != ATTN_KERNEL_KEYGROUPS)
     return ATTN_ERR_UNSUPPORTED;
   const int prev = g_bf16_kernel;
   g_bf16_kernel = which;

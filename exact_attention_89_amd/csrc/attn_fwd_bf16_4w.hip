@@ -48,21 +48,22 @@
 namespace attn89 {
 namespace {
 
-template <int D>
+template <int D, int RW = 4>
 struct Cfg {
-  static constexpr int BR = 128;                 // query rows per workgroup
+  static constexpr int BR = 32 * RW;             // query rows per workgroup (RW waves of 32)
   static constexpr int BC = 64;                  // keys per tile
-  static constexpr int NT = 256;                 // threads per workgroup (4 waves)
+  static constexpr int NT = 64 * RW;             // threads per key group
   static constexpr int ROWB = D * 2;             // bytes per K row
   static constexpr int TILE = BC * ROWB;         // bytes per K tile (and per V^T tile)
   static constexpr int VTROWB = BC * 2;          // bytes per V^T row (64 keys)
-  static constexpr int DMA = TILE / 1024 / 4;    // 1 KiB K loads per wave per tile
+  static constexpr int DMA = TILE / 1024 / RW;   // 1 KiB K loads per wave per tile
   static constexpr int V_UNITS = (BC / 4) * (D / 8);  // threads staging V (4 keys x 8 dims)
   static constexpr int DSTEPS = D / 16;          // k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
   static constexpr int KBLK = BC / 32;           // 32-key blocks of a tile
   static constexpr int LDS = 4 * TILE;           // K double buffer, V^T double buffer
   static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
+  static_assert((BC / 4) * (D / 8) <= NT || NT == 256, "V staging: one unit a thread");
 };
 
 // PRE: scale <= 0, so scores are scaled before they are masked (a separate
@@ -72,15 +73,31 @@ struct Cfg {
 // VARLEN: packed variable-length sequences (FwdArgs cu_q, cu_k): Q, K, V and O are
 // [tokens][H][D], sequence b owns tokens [cu[b], cu[b+1]), rows are H*D apart; Nq
 // and Nk are the longest sequence lengths the grid and the checks were sized for.
-template <int D, bool PRE, bool SPLIT, bool VARLEN>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
+// KS, RW: key groups per workgroup and row waves per group.  The plain kernel is
+// KS = 1, RW = 4 (four waves, 128 rows).  With KS > 1 the workgroup has KS groups of
+// RW waves; every group covers the same 32*RW query rows, group g takes the key tiles
+// t = g, g + KS, ... (each group with its own K / V^T double buffers), and at the end
+// groups 1 .. KS-1 hand their (O, m, l) to group 0 through LDS, where they are combined
+// with the same rescaling as any reference move.  For grids too small to fill the GPU:
+// KS = 2, RW = 4 halves the sequential key loop of a 128-row block (D = 128); KS = 2,
+// RW = 2 (D = 64) also halves the rows of a block, so two workgroups share a CU and the
+// heavy causal blocks spread over twice as many CUs.
+template <int D, bool PRE, bool SPLIT, bool VARLEN, int KS, int RW>
+__global__ __launch_bounds__(64 * RW * KS, KS == 1 ? 2 : (64 * RW * KS >= 512 ? 1 : 2))
+void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   static_assert(!(SPLIT && VARLEN), "split keys over packed sequences is not provided");
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
-  lds_u8* const lds = (lds_u8*)smem;
-
+  static_assert(KS == 1 || (!SPLIT && !VARLEN), "key groups only in the plain kernel");
+  static_assert(RW == 4 || KS > 1, "fewer row waves only with key groups");
+  static_assert(KS * RW <= 8, "at most 8 waves a workgroup");
+  using C = Cfg<D, RW>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS * KS];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform values in scalar registers (branches on them must be real branches:
+  // every wave meets every barrier)
+  const int wave = KS == 1 ? (tid >> 6) : (__builtin_amdgcn_readfirstlane(tid >> 6) % RW);
+  const int kgrp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / RW;   // key group
+  const int tid_g = tid % C::NT;                   // thread inside its key group
+  lds_u8* const lds = (lds_u8*)smem + kgrp * C::LDS;
   const int lane = tid & 63;
   const int lq = lane & 31;   // query column inside the wave's 32 rows
   const int lg = lane >> 5;   // half of the wave
@@ -101,6 +118,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     const int x = wg_id % 8, slot = wg_id / 8;
     bh = x + 8 * (slot / n_qb);
     qb = n_qb - 1 - slot % n_qb;
+  } else if (KS > 1 && KS * RW * 64 * 2 <= 512) {
+    // two workgroups per CU, all resident at once (the dispatcher places workgroups
+    // t and t + grid/2 on the same CU): the first half of the grid takes the causal
+    // blocks longest first, the second half shortest first, so the two workgroups of a
+    // CU add up to about the same work on every CU
+    const int s = wg_id / BH, half = (n_qb + 1) / 2;
+    bh = wg_id % BH;
+    qb = s < half ? n_qb - 1 - s : s - half;
   } else {
     qb = n_qb - 1 - wg_id / BH;
     bh = wg_id % BH;
@@ -181,8 +206,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   // Thread (kg, dg) holds keys 4kg..4kg+3 x dimensions 8dg..8dg+7 (four 16-byte
   // loads) and writes them as 8 rows of V^T, 4 keys (8 bytes) each.
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, kv_bytes);
-  const bool v_owner = C::V_UNITS >= C::NT || tid < C::V_UNITS;
-  const int vkg = tid % (C::BC / 4), vdg = tid / (C::BC / 4);
+  const bool v_owner = C::V_UNITS >= C::NT || tid_g < C::V_UNITS;
+  const int vkg = tid_g % (C::BC / 4), vdg = tid_g / (C::BC / 4);
   const unsigned vgoff = ((unsigned)(4 * vkg) * ld + 8 * vdg) * 2;
   unsigned vwoff[4];  // V^T byte offset of row 8dg + 2x (row 8dg + 2x + 1: + VTROWB)
 #pragma unroll
@@ -265,14 +290,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   const float c_exp = p.c_exp;
 
   // ---- one key tile; PAR = t & 1 selects the buffers at compile time ----
-  auto iteration = [&](const int t, auto par_tag, auto last_tag, auto mask_tag) {
+  auto iteration = [&](const int t, auto par_tag, auto last_tag, auto mask_tag,
+                       const int tstep = 1) {
     constexpr bool MASKED = decltype(mask_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
     constexpr bool LAST = decltype(last_tag)::value;
-    // a) prefetch the next tile
+    // a) prefetch the next tile of this workgroup (key group)
     if (!LAST) {
-      load_k(t + 1, PAR ^ 1);
-      load_v(t + 1);
+      load_k(t + tstep, PAR ^ 1);
+      load_v(t + tstep);
     }
     // b) scores; c) mask
     f32x16 scur[C::KBLK];
@@ -334,40 +360,113 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][j], oacc[d], 0, 0, 0);
         }
     // g) V(t+1) into V^T buffer PAR^1; the next tile must be in LDS before any wave
-    //    goes on
+    //    goes on (with key groups the caller holds the barrier, met by every group)
     if (!LAST) {
       store_v(PAR ^ 1);
-      __syncthreads();
+      if (KS == 1) __syncthreads();
     }
   };
 
-  // ---- prologue: K(t_begin) and V(t_begin) in LDS ----
-  if (n_tiles > t_begin) {
-    load_v(t_begin);
-    load_k(t_begin, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
-  if (n_tiles > t_begin) store_v(0);
-  __syncthreads();
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using T_ = std::true_type;
   using F_ = std::false_type;
-  int t = t_begin;
-  // tiles every row of the workgroup sees whole: no mask code at all
-  for (; t + 2 < n_tiles && t + 1 < n_full; t += 2) {
-    iteration(t, I0{}, F_{}, F_{});
-    iteration(t + 1, I1{}, F_{}, F_{});
-  }
-  for (; t + 2 < n_tiles; t += 2) {
-    iteration(t, I0{}, F_{}, T_{});
-    iteration(t + 1, I1{}, F_{}, T_{});
-  }
-  if (t + 1 < n_tiles) {
-    iteration(t, I0{}, F_{}, T_{});
-    iteration(t + 1, I1{}, T_{}, T_{});
-  } else if (t < n_tiles) {
-    iteration(t, I0{}, T_{}, T_{});
+  if constexpr (KS == 1) {
+    // ---- prologue: K(t_begin) and V(t_begin) in LDS ----
+    if (n_tiles > t_begin) {
+      load_v(t_begin);
+      load_k(t_begin, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
+    if (n_tiles > t_begin) store_v(0);
+    __syncthreads();
+    int t = t_begin;
+    // tiles every row of the workgroup sees whole: no mask code at all
+    for (; t + 2 < n_tiles && t + 1 < n_full; t += 2) {
+      iteration(t, I0{}, F_{}, F_{});
+      iteration(t + 1, I1{}, F_{}, F_{});
+    }
+    for (; t + 2 < n_tiles; t += 2) {
+      iteration(t, I0{}, F_{}, T_{});
+      iteration(t + 1, I1{}, F_{}, T_{});
+    }
+    if (t + 1 < n_tiles) {
+      iteration(t, I0{}, F_{}, T_{});
+      iteration(t + 1, I1{}, T_{}, T_{});
+    } else if (t < n_tiles) {
+      iteration(t, I0{}, T_{}, T_{});
+    }
+  } else {
+    // group kgrp: tiles my_first, my_first + KS, ...; every group runs n_steps steps
+    // (a group past its last tile only meets the barriers)
+    const int my_first = t_begin + kgrp;
+    const int n_steps = (n_tiles - t_begin + KS - 1) / KS;
+    if (my_first < n_tiles) {
+      load_v(my_first);
+      load_k(my_first, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (my_first < n_tiles) store_v(0);
+    __syncthreads();
+    auto step = [&](int i, auto par_tag) {
+      const int t = my_first + KS * i;
+      const bool more = i + 1 < n_steps;            // uniform over the workgroup
+      if (t < n_tiles) {
+        if (t + KS < n_tiles) iteration(t, par_tag, F_{}, T_{}, KS);
+        else iteration(t, par_tag, T_{}, T_{}, KS);
+      }
+      if (more) __syncthreads();
+    };
+    for (int i = 0; i < n_steps; i += 2) {
+      step(i, I0{});
+      if (i + 1 < n_steps) step(i + 1, I1{});
+    }
+    // hand the (O, m, l) of groups 1 .. KS-1 to group 0: each group's own LDS region
+    // takes its O, group 0's region the row statistics (every region is free once all
+    // groups have left the loop)
+    __syncthreads();
+    float* s_x = (float*)smem;
+    const int slot = wave * 64 + lane;             // < 64 * RW
+    if (kgrp > 0) {
+      float* o_x = (float*)((lds_u8*)smem + kgrp * C::LDS);
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o_x[(d * 16 + r) * C::NT + slot] = oacc[d][r];
+      float* st = s_x + (kgrp - 1) * 3 * C::NT;
+      st[slot] = m_run;
+      st[C::NT + slot] = m_use;
+      st[2 * C::NT + slot] = l_run;
+    }
+    __syncthreads();
+    if (kgrp > 0) return;                           // no barrier follows
+    float M = m_run;
+#pragma unroll
+    for (int g = 1; g < KS; ++g) M = fmaxf(M, s_x[(g - 1) * 3 * C::NT + slot]);
+    if (M != kNegInf) {
+      // every part is rescaled to the largest reference (a part without any valid key
+      // has weight 0), the same correction as a reference move
+      const float f0 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_use - M);
+      l_run *= f0;
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= f0;
+#pragma unroll
+      for (int g = 1; g < KS; ++g) {
+        const float* st = s_x + (g - 1) * 3 * C::NT;
+        const float mg = st[slot], mug = st[C::NT + slot], lg_ = st[2 * C::NT + slot];
+        const float fg = mg == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mug - M);
+        l_run += lg_ * fg;
+        const float* o_x = (const float*)((lds_u8*)smem + g * C::LDS);
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[d][r] += o_x[(d * 16 + r) * C::NT + slot] * fg;
+      }
+      m_run = M;
+      m_use = M;
+    }
   }
 
   // ---- epilogue: O = a / l (0 for rows with no valid key), LSE = ln2 (m + log2 l) ----
@@ -410,36 +509,47 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_4w_kernel(FwdArgs p) {
 
 }  // namespace
 
-template <bool SPLIT, bool VARLEN>
+template <bool SPLIT, bool VARLEN, int KS, int RW>
 static int launch_4w(const FwdArgs& a, int D, hipStream_t stream) {
-  const int n_qb = (a.Nq + 127) / 128;
+  const int n_qb = (a.Nq + 32 * RW - 1) / (32 * RW);
   const long long grid = (long long)n_qb * a.B * a.H * (SPLIT ? a.n_splits : 1);
   if (grid > 0x7fffffffLL) return -8;
-  const dim3 g((unsigned)grid), blk(256);
+  const dim3 g((unsigned)grid), blk(64 * RW * KS);
   if (D == 128) {
-    if (a.pre_scale)
-      attn_fwd_bf16_4w_kernel<128, true, SPLIT, VARLEN><<<g, blk, 0, stream>>>(a);
-    else
-      attn_fwd_bf16_4w_kernel<128, false, SPLIT, VARLEN><<<g, blk, 0, stream>>>(a);
+    if constexpr (RW == 4) {
+      if (a.pre_scale)
+        attn_fwd_bf16_4w_kernel<128, true, SPLIT, VARLEN, KS, RW><<<g, blk, 0, stream>>>(a);
+      else
+        attn_fwd_bf16_4w_kernel<128, false, SPLIT, VARLEN, KS, RW><<<g, blk, 0, stream>>>(a);
+    } else {
+      return -3;   // D = 128 key groups use four row waves
+    }
   } else {
     if (a.pre_scale)
-      attn_fwd_bf16_4w_kernel<64, true, SPLIT, VARLEN><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<64, true, SPLIT, VARLEN, KS, RW><<<g, blk, 0, stream>>>(a);
     else
-      attn_fwd_bf16_4w_kernel<64, false, SPLIT, VARLEN><<<g, blk, 0, stream>>>(a);
+      attn_fwd_bf16_4w_kernel<64, false, SPLIT, VARLEN, KS, RW><<<g, blk, 0, stream>>>(a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
-int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream) {
-  return launch_4w<false, false>(a, D, stream);
+int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream, int key_groups) {
+  if (key_groups == 2) {
+    // D = 64: 64-row blocks, two key groups of two row waves (4 waves, two workgroups
+    // per CU); D = 128: 128-row blocks, two key groups of four row waves (each group's
+    // K / V^T buffers take 64 KiB of LDS, one workgroup per CU)
+    if (D == 64) return launch_4w<false, false, 2, 2>(a, D, stream);
+    return launch_4w<false, false, 2, 4>(a, D, stream);
+  }
+  return launch_4w<false, false, 1, 4>(a, D, stream);
 }
 
 int launch_attn_fwd_bf16_4w_split(const FwdArgs& a, int D, hipStream_t stream) {
-  return launch_4w<true, false>(a, D, stream);
+  return launch_4w<true, false, 1, 4>(a, D, stream);
 }
 
 int launch_attn_fwd_bf16_4w_varlen(const FwdArgs& a, int D, hipStream_t stream) {
-  return launch_4w<false, true>(a, D, stream);
+  return launch_4w<false, true, 1, 4>(a, D, stream);
 }
 
 }  // namespace attn89

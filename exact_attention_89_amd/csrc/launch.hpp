@@ -10,9 +10,10 @@
 namespace attn89 {
 
 // bf16 forward kernels: 8-wave ping-pong workgroups of 256 query rows (D = 128 only)
-// and 4-wave workgroups of 128 rows (any supported D).
+// and 4-wave workgroups of 128 rows (any supported D); key_groups = 2 gives the latter
+// 8 waves that split each row block's key tiles between two groups.
 int launch_attn_fwd_bf16_pp(const FwdArgs& a, int D, hipStream_t stream);
-int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream);
+int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream, int key_groups = 1);
 // 4-wave kernel over one key range per workgroup (FwdArgs n_splits, kv_chunk,
 // o_part, lse_part), partial results only
 int launch_attn_fwd_bf16_4w_split(const FwdArgs& a, int D, hipStream_t stream);

@@ -76,19 +76,32 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const int32_t* kv_lens, void* stream);
 
 /*
- * attn_fwd_select_kernel -- which of the two forward kernels attn_fwd (bf16) and
- * attn_fwd_fp8 (E4M3) launch.  For each input type both kernels compute the same
- * function with the same arithmetic (bitwise identical results); they differ only in
- * how work is spread over the GPU:
+ * attn_fwd_select_kernel -- which forward kernel attn_fwd (bf16) and attn_fwd_fp8
+ * (E4M3) launch.  For each input type the ping-pong and four-wave kernels compute the
+ * same function with the same arithmetic (bitwise identical results); they differ
+ * only in how work is spread over the GPU:
  *
  *   ATTN_KERNEL_PINGPONG  8-wave workgroups of 256 query rows, two wave groups
  *                         half a key tile apart (one on the matrix cores while
  *                         the other computes its softmax); one workgroup per CU
  *   ATTN_KERNEL_FOURWAVE  4-wave workgroups of 128 query rows, two per CU
+ *   ATTN_KERNEL_KEYGROUPS (bf16 only) 8-wave workgroups of 128 query rows whose two
+ *                         4-wave groups take alternate key tiles of the same rows
+ *                         and combine their partial results at the end (page
+ *                         "Attention softmax fusion", section "The tile loop": the
+ *                         rescaling by exp(m_old - m_new) joins any two parts);
+ *                         half the sequential key loop per workgroup, for grids
+ *                         too small to fill the GPU.  Same function and tolerance,
+ *                         a different summation order (not bitwise equal to the
+ *                         others); attn_fwd_fp8 treats it as FOURWAVE
  *   ATTN_KERNEL_AUTO      (default) attn_fwd: ping-pong when D = 128, Nq >= 256
  *                         and its grid, ceil(Nq/256)*B*H workgroups, covers every
- *                         compute unit, otherwise four-wave; attn_fwd_fp8:
- *                         four-wave (the faster one for FP8 at every measured shape)
+ *                         compute unit; otherwise key groups when ceil(Nq/128)*B*H
+ *                         is at most the number of compute units (one four-wave
+ *                         workgroup per CU would leave half of each CU idle and
+ *                         the longest key loop alone would set the time); otherwise
+ *                         four-wave.  attn_fwd_fp8: four-wave (the faster one for
+ *                         FP8 at every measured shape)
  *
  * The setting is process-wide and not synchronised: change it only while no
  * other thread calls attn_fwd.  Returns the previous setting, or
@@ -97,6 +110,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 #define ATTN_KERNEL_AUTO      0
 #define ATTN_KERNEL_PINGPONG  1
 #define ATTN_KERNEL_FOURWAVE  2
+#define ATTN_KERNEL_KEYGROUPS 3
 int attn_fwd_select_kernel(int which);
 
 /*

@@ -34,11 +34,12 @@ def _gpu():
     api.load_library()
 
 
-@pytest.fixture(params=["pingpong", "fourwave"])
+@pytest.fixture(params=["pingpong", "fourwave", "keygroups"])
 def bf16_kernel(request):
-    """Run a bf16 test on each of the two forward kernels (forced, not auto-picked)."""
+    """Run a bf16 test on each of the three forward kernels (forced, not auto-picked)."""
     which = {"pingpong": api.ATTN_KERNEL_PINGPONG,
-             "fourwave": api.ATTN_KERNEL_FOURWAVE}[request.param]
+             "fourwave": api.ATTN_KERNEL_FOURWAVE,
+             "keygroups": api.ATTN_KERNEL_KEYGROUPS}[request.param]
     prev = api.attn_fwd_select_kernel(which)
     _say(f"[parity] bf16 kernel: {request.param}")
     yield request.param
