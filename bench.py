@@ -42,9 +42,10 @@ def log(msg):
 
 
 def kernel_source_hash():
-    """Hash of the bf16 kernel sources: a traffic record taken from other sources is stale."""
-    from exact_attention_89_amd.traffic import _kernel_hash
-    return _kernel_hash()
+    """Hash of the throughput kernel's sources: a traffic record taken from other sources
+    is stale."""
+    from exact_attention_89_amd.traffic import _headline_hash
+    return _headline_hash()
 
 
 def measured_traffic(workload):
@@ -492,6 +493,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--clock-trace", default=None,
                     help="write the shader-clock samples (JSON) to this path")
+    ap.add_argument("--kernel", choices=["auto", "pingpong", "fourwave", "keygroups"],
+                    default="auto",
+                    help="bf16 forward kernel attn_fwd launches (attn_fwd_select_kernel)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="calls timed with a 512 MiB buffer written before each (0: skip)")
     ap.add_argument("--op", choices=["attention", "partial", "materialized", "softmax_rows",
@@ -544,6 +548,9 @@ def main():
         from exact_attention_89_amd import build
         build.build()
     api.load_library()
+    api.attn_fwd_select_kernel({"auto": api.ATTN_KERNEL_AUTO, "pingpong": api.ATTN_KERNEL_PINGPONG,
+                                "fourwave": api.ATTN_KERNEL_FOURWAVE,
+                                "keygroups": api.ATTN_KERNEL_KEYGROUPS}[args.kernel])
     dev = torch.device("cuda:0")
     qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
     ld = None if lens is None else torch.from_numpy(lens).to(dev)
@@ -677,7 +684,7 @@ def main():
               "causal": w.causal, "seed": w.seed,
               "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
               "launch_ms": launch_stats, "cold": cold, "clock": clocks, "check": check,
-              "versions": versions(torch)}
+              "kernel": args.kernel, "versions": versions(torch)}
     if lens is not None:
         # key padding: the metric counts every key slot; the work that exists is the
         # valid keys, 4*H*Nq*D*sum(kv_len) (halved when causal)
