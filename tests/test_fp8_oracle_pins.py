@@ -193,3 +193,59 @@ def test_quantizer_round_trip():
     step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(np.abs(t), 2.0 ** -9))), -6) - 3)
     assert np.all(np.abs(y - t) <= step / 2 + 1e-12)
     assert np.max(np.abs(y)) == 448.0
+
+
+def _kernel_model(q8, k8, v8, ds, scale, causal):
+    """A float32 model of the FP8 kernel's arithmetic for one (batch, head), on the CPU:
+    fp32 scores of the decoded codes, 64-key tiles, an exponent reference that moves only
+    when the tile maximum exceeds it by more than 2 (log2 units), weights 2^6 exp2(x)
+    rounded to E4M3 by torch's cast before the value product, the normaliser over the
+    unrounded weights, O = v_descale acc / l."""
+    f32 = np.float32
+    q = oracle.e4m3_decode(q8).astype(f32)
+    k = oracle.e4m3_decode(k8).astype(f32)
+    v = oracle.e4m3_decode(v8).astype(f32)
+    c = f32(f32(f32(scale) * f32(ds[0])) * f32(ds[1])) * f32(1.4426950408889634)
+    s = (q @ k.T).astype(f32)
+    nq, nk = s.shape
+    if causal:
+        s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None], s, f32(-np.inf))
+    m = np.full(nq, -np.inf, f32)
+    l = np.zeros(nq, f32)
+    acc = np.zeros((nq, v.shape[1]), f32)
+    for lo in range(0, nk, 64):
+        blk = s[:, lo:lo + 64] * c
+        mx = blk.max(axis=1)
+        move = mx > m + f32(2)
+        m_new = np.where(move, mx, m)
+        m_use = np.where(m_new == -np.inf, f32(0), m_new)
+        alpha = np.where(move, np.exp2(m - m_use), f32(1)).astype(f32)
+        l *= alpha
+        acc *= alpha[:, None]
+        m = m_new
+        w = np.exp2(blk - (m_use - f32(6))[:, None]).astype(f32)
+        l += w.sum(axis=1, dtype=f32)
+        wr = torch.from_numpy(w).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+        acc += wr @ v[lo:lo + 64]
+    return (f32(ds[2]) * acc / l[:, None]).astype(np.float64)
+
+
+@pytest.mark.parametrize("nq,nk,d,causal,std", [(64, 4096, 128, False, 1.0),
+                                                (96, 1000, 64, True, 1.0),
+                                                (32, 2048, 128, False, 3.0)])
+def test_o_bound_covers_a_model_of_the_kernel_arithmetic(nq, nk, d, causal, std):
+    """The element-wise FP8 bound of the parity tests holds for a float32 model of the
+    kernel's steps (the rounding of the weights to E4M3 dominates), and is not loose: the
+    model's error reaches a visible fraction of it."""
+    from tests.parity import fp8_o_bound, fp8_score_abs
+
+    q8, k8, v8, ds = random_fp8_case(11, 1, 1, nq, nk, d, std=std)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, _, P = oracle.attention_fp8_oracle(q8, k8, v8, scale, *ds, causal=causal,
+                                              return_probs=True)
+    o_model = _kernel_model(q8[0, 0], k8[0, 0], v8[0, 0], ds, scale, causal)
+    sa = fp8_score_abs(oracle.dequantize(q8, ds[0]), oracle.dequantize(k8, ds[1]), scale)
+    bound = fp8_o_bound(P, oracle.dequantize(v8, ds[2]), o_ref, sa)[0, 0]
+    ratio = np.abs(o_model - o_ref[0, 0]) / bound
+    assert ratio.max() <= 1.0
+    assert ratio.max() >= 0.02

@@ -16,7 +16,7 @@ import pytest
 import oracle
 from exact_attention_89_amd import api
 from exact_attention_89_amd.workloads import WORKLOADS, generate_fp8, random_fp8_case
-from tests.parity import check_fp8, fp8_o_bound
+from tests.parity import check_fp8, fp8_o_bound, fp8_score_abs
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -67,7 +67,8 @@ def _run(B, H, Nq, Nk, D, causal=False, lens=None, seed=0, std=1.0, scale=None, 
     o, lse = _gpu_fp8(q8, k8, v8, ds, scale, causal, lens)
     o_ref, lse_ref, P = oracle.attention_fp8_oracle(q8, k8, v8, scale, *ds, causal=causal,
                                                     kv_lens=lens, return_probs=True)
-    bound = fp8_o_bound(P, oracle.dequantize(v8, ds[2]), o_ref)
+    sa = fp8_score_abs(oracle.dequantize(q8, ds[0]), oracle.dequantize(k8, ds[1]), scale)
+    bound = fp8_o_bound(P, oracle.dequantize(v8, ds[2]), o_ref, sa)
     res = check_fp8(o, lse, o_ref, lse_ref, bound, what)
     _say(f"[fp8]   max|dO| {res[0]:.3e}  max|dO|/bound {res[1]:.3f}  rms {res[2]:.3e}  "
          f"LSE {res[3]:.2e}")
@@ -194,7 +195,8 @@ def test_fp8_headline_shape_sampled_rows():
             valid = oracle.valid_keys(i, i + 1, w.Nk, True, w.Nk)
             o_ref, lse_ref, P = oracle.attention_rows(Q[0, h, i:i + 1], K[0, h], V[0, h], sigma,
                                                       valid, return_probs=True)
-            bound = fp8_o_bound(P, V[0, h], o_ref)
+            bound = fp8_o_bound(P, V[0, h], o_ref,
+                                fp8_score_abs(Q[0, h, i:i + 1], K[0, h], w.scale))
             res = check_fp8(o[0, h, i:i + 1], lse[0, h, i:i + 1], o_ref, lse_ref, bound,
                             f"fp8 headline h={h} i={i}")
             worst = max(worst, res[1])

@@ -11,7 +11,7 @@ import pytest
 import oracle
 from exact_attention_89_amd import api
 from exact_attention_89_amd.workloads import quantize_e4m3, round_to_bf16
-from tests.parity import check, check_fp8, fp8_o_bound
+from tests.parity import check, check_fp8, fp8_o_bound, fp8_score_abs
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -73,7 +73,8 @@ def test_fp8_two_million_keys(big):
     torch.cuda.synchronize()
     o_ref, lse_ref, P = oracle.attention_fp8_oracle(q8, k8, v8, 0.09, qd, kd, vd,
                                                     return_probs=True)
-    bound = fp8_o_bound(P, oracle.dequantize(v8, vd), o_ref)
+    sa = fp8_score_abs(oracle.dequantize(q8, qd), oracle.dequantize(k8, kd), 0.09)
+    bound = fp8_o_bound(P, oracle.dequantize(v8, vd), o_ref, sa)
     check_fp8(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, bound, "large fp8")
 
 
