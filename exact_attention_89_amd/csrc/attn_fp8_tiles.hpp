@@ -69,12 +69,16 @@ __device__ __forceinline__ u32x4 transpose4x4_bytes(unsigned w0, unsigned w1, un
 // round-to-nearest-even, bytes 0..3 = s0..s3; their fp32 sum is added to lsum
 __device__ __forceinline__ int exp2_pack_e4m3(float s0, float s1, float s2, float s3, float c,
                                               float m_sh, float& lsum) {
-  const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m_sh));
+  const float x0 = __builtin_fmaf(s0, c, -m_sh);
+  const float e0 = __builtin_amdgcn_exp2f(x0);
   const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m_sh));
   const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2, c, -m_sh));
   const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s3, c, -m_sh));
   lsum += (e0 + e1) + (e2 + e3);
-  const int word = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+  // The first conversion writes bytes 0-1 and keeps bytes 2-3 of its third operand,
+  // which the second conversion overwrites: any dead register serves (here x0), so
+  // the compiler needs no zeroed register for it.
+  const int word = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, __float_as_int(x0), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, word, true);
 }
 
