@@ -35,6 +35,20 @@ __device__ __forceinline__ int kswz8(int row) {
 // V^T rows are 64 bytes (4 chunks): four rows span the banks.
 __device__ __forceinline__ int vtswz8(int d) { return (d >> 2) & 3; }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b8: 8 bytes per lane, transposed across each group of 16 lanes: lane
+// 16g + 8h + j receives, as its byte m, byte j of the 8 bytes at the address given by
+// lane 16g + h + 2m (measured on gfx950 with a probe that reads back tagged LDS bytes)
+__device__ __forceinline__ i32x2 lds_tr8(const lds_u8* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2*)(const_cast<lds_u8*>(p)));
+}
+
+__device__ __forceinline__ i32x8 join_tr8(i32x2 a, i32x2 b, i32x2 c, i32x2 d) {
+  return (i32x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 __device__ __forceinline__ i32x8 join32(u32x4 lo, u32x4 hi) {
   return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};

@@ -28,14 +28,17 @@
 // accumulator of 32 keys x 32 queries leaves register r of lane l with key
 // 8*(r/4) + 4*(l/32) + r%4 and query l%32, so the 64 P values of a lane (two 32-key
 // blocks) are exactly the 32 bytes one B operand of O^T = V^T P^T needs: byte
-// 16*kb + r of lane half h is key 32*kb + 8*(r/4) + 4*h + r%4.  The V^T tile in LDS
-// stores each dimension's 64 keys in that order (position 32*h + 16*kb + 4*(r/4) +
-// r%4), so the A operand of a lane is 32 consecutive bytes of one V^T row.
+// 16*kb + r of lane half h is key 32*kb + 8*(r/4) + 4*h + r%4.  The A operand of
+// O^T = V^T P^T (one dimension per lane, its 64 keys in that byte order) is read from
+// the row-major V tile with four transposing LDS reads (ds_read_b64_tr_b8), whose lane
+// addresses pick the keys in the P byte order.
 //
-// Data movement.  K tiles go global -> LDS by buffer_load ... lds (row-major, 16-byte
-// chunks XOR-swizzled by row); V tiles pass through registers, are transposed with
-// byte permutes and written as V^T (chunks swizzled by row).  Both double buffered;
-// the key loop is unrolled by two so every LDS offset is an immediate.
+// Data movement.  K and V tiles both go global -> LDS by buffer_load ... lds
+// (row-major, 16-byte chunks XOR-swizzled by row), double buffered, no registers and
+// no vector instructions; the key loop is unrolled by two so every LDS offset is an
+// immediate.  (Staging V through registers and transposing it with byte permutes cost
+// 16 vector instructions per tile and thread, in a kernel whose vector unit is the
+// bottleneck; the transposing reads replaced them: +8 % at B=1 H=32 N=8192 causal.)
 #include <type_traits>
 
 #include "attn_fp8_tiles.hpp"
@@ -51,13 +54,11 @@ struct Cfg8 {
   static constexpr int NT = 256;                 // threads per workgroup
   static constexpr int ROWB = D;                 // bytes per K row
   static constexpr int TILE = BC * D;            // bytes per K tile (and per V^T tile)
-  static constexpr int VTROWB = BC;              // bytes per V^T row
   static constexpr int DMA = TILE / 1024 / 4;    // 1 KiB K loads per wave per tile
-  static constexpr int V_UNITS = (BC / 4) * (D / 8);  // threads staging V (4 keys x 8 dims)
   static constexpr int DSTEPS = D / 64;          // k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
-  static constexpr int LDS = 4 * TILE;           // K double buffer, V^T double buffer
-  static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
+  static constexpr int LDS = 4 * TILE;           // K double buffer, V double buffer
+  static constexpr int VT0 = 2 * TILE;           // offset of the V buffers
 };
 
 // PRE: scale <= 0, scores are scaled before they are masked.
@@ -130,43 +131,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
                            koff[n], t * C::BC * D);
   };
 
-  // ---- V: global -> registers -> LDS as V^T in the P byte order ----
-  // Thread (kg, dg) holds keys 4kg .. 4kg+3 x dimensions 8dg .. 8dg+7 and writes 8
-  // dwords, one per dimension, each the 4 keys' bytes.  Keys 4kg .. 4kg+3 sit at
-  // positions 4*(8h + 4kb + g) .. + 3 of a V^T row, with kb = kg/8, g = (kg%8)/2,
-  // h = kg%2: dword g of logical chunk 2h + kb.
+  // ---- V: global -> LDS without registers, row-major like K ----
+  // The P.V operand (V^T: 32 dimensions x 64 keys per lane group, in the P byte order)
+  // is read back with the transposing ds_read_b64_tr_b8: in each group of 16 lanes, the
+  // lane 16g + 8h + j receives, as byte m of its 8, byte j of the 8 bytes at the address
+  // of lane 16g + h + 2m.  So the lane that holds position i of its group addresses, in
+  // read q, key 16q + 8(m/4) + 4(g/2) + m%4 (m = i/2: the key whose P byte sits at
+  // position 8q + m of lane half g/2) at dimensions 16(g%2) + 8(i%2) .. + 8 of the
+  // 32-dimension block: four reads give a lane its 32 operand bytes.
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (unsigned)L * D);
-  const bool v_owner = C::V_UNITS >= C::NT || tid < C::V_UNITS;
-  const int vkg = tid % (C::BC / 4), vdg = tid / (C::BC / 4);
-  const unsigned vgoff = (unsigned)(4 * vkg) * D + 8 * vdg;
-  unsigned vwoff[2];  // V^T byte offset of dimension 8dg + 4i (dimension 8dg + 4i + x: + x rows)
-  const int vchunk = 2 * (vkg & 1) + (vkg >> 3);
-  const int vdw = (vkg >> 1) & 3;
+  auto load_v = [&](int t, int stage) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int d = 8 * vdg + 4 * i;
-    // vtswz8(d + x) = vtswz8(d) for x < 4 (d is a multiple of 4)
-    vwoff[i] = d * C::VTROWB + ((vchunk ^ vtswz8(d)) * 16) + 4 * vdw;
+    for (int n = 0; n < C::DMA; ++n)
+      buffer_load16_to_lds(vrs,
+                           (lds_void*)(lds + C::VT0 + stage * C::TILE + (wave * C::DMA + n) * 1024),
+                           koff[n], t * C::BC * D);
+  };
+  unsigned vtr[C::DBLK];   // read q of 32-dimension block d: vtr[d] + 16 q rows
+  {
+    const int gi = lane & 15, gg = lane >> 4, m = gi >> 1;
+    const int key = 8 * (m >> 2) + 4 * (gg >> 1) + (m & 3);   // + 16 q (same swizzle)
+#pragma unroll
+    for (int d = 0; d < C::DBLK; ++d)
+      vtr[d] = key * C::ROWB + (((2 * d + (gg & 1)) ^ kswz8<D>(key)) * 16) + 8 * (gi & 1);
   }
-  u32x2 vreg[4];
-  auto load_v = [&](int t) {
-    if (v_owner) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[r] = buffer_load8_so(vrs, vgoff + r * D, t * C::BC * D);
-    }
-  };
-  auto store_v = [&](int buf) {
-    if (v_owner) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const u32x4 d4 = transpose4x4_bytes(vreg[0][i], vreg[1][i], vreg[2][i], vreg[3][i]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          *(__attribute__((address_space(3))) unsigned*)(
-              lds + C::VT0 + buf * C::TILE + vwoff[i] + x * C::VTROWB) = d4[x];
-      }
-    }
-  };
 
   // ---- fragment read offsets ----
   // K: row lq of each 32-key block, logical chunks 4s + 2lg and 4s + 2lg + 1
@@ -176,10 +164,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
 #pragma unroll
     for (int c = 0; c < 2; ++c)
       kro[s][c] = lq * C::ROWB + (((4 * s + 2 * lg + c) ^ kswz8<D>(lq)) * 16);
-  // V^T: row lq of each 32-dimension block, logical chunks 2lg and 2lg + 1
-  unsigned vro[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) vro[c] = lq * C::VTROWB + (((2 * lg + c) ^ vtswz8(lq)) * 16);
 
   auto qk = [&](int stage, f32x16* sacc) {
 #pragma unroll
@@ -222,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     constexpr bool MASKED = decltype(mask_tag)::value;
     if (!LAST) {
       load_k(t + 1, PAR ^ 1);
-      load_v(t + 1);
+      load_v(t + 1, PAR ^ 1);
     }
     f32x16 scur[2];
     qk(PAR, scur);
@@ -262,22 +246,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     // O^T += V^T P^T
 #pragma unroll
     for (int d = 0; d < C::DBLK; ++d) {
-      const lds_u8* base = lds + C::VT0 + PAR * C::TILE + d * 32 * C::VTROWB;
-      const i32x8 va = join32(lds_load<u32x4>(base, vro[0]), lds_load<u32x4>(base, vro[1]));
+      const lds_u8* base = lds + C::VT0 + PAR * C::TILE + vtr[d];
+      const i32x8 va = join_tr8(lds_tr8(base), lds_tr8(base + 16 * C::ROWB),
+                                lds_tr8(base + 32 * C::ROWB), lds_tr8(base + 48 * C::ROWB));
       oacc[d] = mfma_fp8(va, pf, oacc[d]);
     }
-    if (!LAST) {
-      store_v(PAR ^ 1);
-      __syncthreads();
-    }
+    if (!LAST) __syncthreads();
   };
 
   if (n_tiles > 0) {
-    load_v(0);
+    load_v(0, 0);
     load_k(0, 0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
-  if (n_tiles > 0) store_v(0);
   __syncthreads();
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
