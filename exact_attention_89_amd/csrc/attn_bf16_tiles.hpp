@@ -74,6 +74,30 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Swizzle of the 16-byte chunks of a row-major V tile (4-wave kernel): row bits 0-1
+// select the 64-byte window, so a transposing read that gathers four consecutive keys
+// touches four windows; it does not change when the row moves by a multiple of 4.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return D == 128 ? 4 * (row & 3) : 2 * (row & 3);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: 8 bytes (four 16-bit elements) per lane, transposed across each
+// group of 16 lanes: lane 16g + 4a + j receives, as its element m, element j of the
+// four at the address given by lane 16g + a + 4m (measured on gfx950 with a probe that
+// reads back tagged LDS elements)
+__device__ __forceinline__ i16x4 lds_tr16(const lds_u8* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<lds_u8*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 join_tr16(i16x4 lo, i16x4 hi) {
+  const i16x4 v[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }

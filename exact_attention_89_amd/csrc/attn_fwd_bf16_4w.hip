@@ -55,9 +55,7 @@ struct Cfg {
   static constexpr int NT = 64 * RW;             // threads per key group
   static constexpr int ROWB = D * 2;             // bytes per K row
   static constexpr int TILE = BC * ROWB;         // bytes per K tile (and per V^T tile)
-  static constexpr int VTROWB = BC * 2;          // bytes per V^T row (64 keys)
   static constexpr int DMA = TILE / 1024 / RW;   // 1 KiB K loads per wave per tile
-  static constexpr int V_UNITS = (BC / 4) * (D / 8);  // threads staging V (4 keys x 8 dims)
   static constexpr int DSTEPS = D / 16;          // k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
   static constexpr int KBLK = BC / 32;           // 32-key blocks of a tile
@@ -202,40 +200,41 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
                            koff[n], t * C::BC * ld * 2);
   };
 
-  // ---- V: global -> registers -> LDS, transposed ----
-  // Thread (kg, dg) holds keys 4kg..4kg+3 x dimensions 8dg..8dg+7 (four 16-byte
-  // loads) and writes them as 8 rows of V^T, 4 keys (8 bytes) each.
+  // ---- V: global -> LDS without registers, row-major ----
+  // The P.V operand (one dimension per lane, the 8 keys of its P fragment) is read back
+  // with the transposing ds_read_b64_tr_b16 (see lds_tr16): the lane at position
+  // i = 4m + a of a group of 16 lanes (group g) addresses, in read q, key
+  // 8(g/2) + 4q + m (plus the P.V step's 16-key offset) at dimensions
+  // 16(g%2) + 4a .. + 4 of the 32-dimension block, so two reads give a lane its 8
+  // elements.  V rows keep their 16-byte chunks XOR-swizzled by vswz(row), which
+  // depends on row bits 0-1 only: the four keys one read gathers then fall in different
+  // 64-byte windows (no bank conflicts), and key offsets of 4, 16 and 32 keep the
+  // swizzle, so they are immediate offsets.
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, kv_bytes);
-  const bool v_owner = C::V_UNITS >= C::NT || tid_g < C::V_UNITS;
-  const int vkg = tid_g % (C::BC / 4), vdg = tid_g / (C::BC / 4);
-  const unsigned vgoff = ((unsigned)(4 * vkg) * ld + 8 * vdg) * 2;
-  unsigned vwoff[4];  // V^T byte offset of row 8dg + 2x (row 8dg + 2x + 1: + VTROWB)
+  unsigned voff[C::DMA];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int d = 8 * vdg + 2 * x;
-    vwoff[x] = d * C::VTROWB + (((vkg >> 1) ^ vtswz(d)) * 16) + (vkg & 1) * 8;
+  for (int n = 0; n < C::DMA; ++n) {
+    const int byte = (wave * C::DMA + n) * 1024 + 16 * lane;
+    const int row = byte / C::ROWB;
+    const int ch = ((byte % C::ROWB) / 16) ^ vswz<D>(row);
+    voff[n] = ((unsigned)row * ld + 8 * ch) * 2;
   }
-  u32x4 vreg[4];
-  auto load_v = [&](int t) {
-    if (v_owner) {
+  auto load_v = [&](int t, int stage) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = buffer_load16_so(vrs, vgoff + r * ld * 2, t * C::BC * ld * 2);
-    }
+    for (int n = 0; n < C::DMA; ++n)
+      buffer_load16_to_lds(vrs,
+                           (lds_void*)(lds + C::VT0 + stage * C::TILE + (wave * C::DMA + n) * 1024),
+                           voff[n], t * C::BC * ld * 2);
   };
-  auto store_v = [&](int buf) {
-    if (v_owner) {
+  unsigned vtr[C::DBLK];   // read q of 32-dimension block d at P.V step s: + (16 s + 4 q) rows
+  {
+    const int gi = lane & 15, gg = lane >> 4, a = gi & 3, m = gi >> 2;
+    const int key = 8 * (gg >> 1) + m;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // row 8dg + e of V^T: dimension e of keys 4kg .. 4kg + 3
-        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const u32x2 pk = {__builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel),
-                          __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel)};
-        *(__attribute__((address_space(3))) u32x2*)(
-            lds + C::VT0 + buf * C::TILE + vwoff[e >> 1] + (e & 1) * C::VTROWB) = pk;
-      }
-    }
-  };
+    for (int d = 0; d < C::DBLK; ++d)
+      vtr[d] = key * C::ROWB + (((4 * d + 2 * (gg & 1) + (a >> 1)) ^ vswz<D>(key)) * 16) +
+               8 * (a & 1);
+  }
 
   // ---- fragment read offsets (per lane, fixed for the whole loop) ----
   const int krow = swap_bits23(lq);   // key (row of K) this lane feeds to the MFMA
@@ -243,10 +242,6 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
 #pragma unroll
   for (int s = 0; s < C::DSTEPS; ++s)
     kro[s] = krow * C::ROWB + (((2 * s + lg) ^ kswz<D>(krow)) * 16);
-  unsigned vro[C::KBLK * 2];
-#pragma unroll
-  for (int x = 0; x < C::KBLK * 2; ++x)
-    vro[x] = lq * C::VTROWB + (((2 * x + lg) ^ vtswz(lq)) * 16);
 
   // S^T = K Q^T for the tile in K buffer `stage`, fp32 accumulation from 0
   auto qk = [&](int stage, f32x16* sacc) {
@@ -298,7 +293,7 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     // a) prefetch the next tile of this workgroup (key group)
     if (!LAST) {
       load_k(t + tstep, PAR ^ 1);
-      load_v(t + tstep);
+      load_v(t + tstep, PAR ^ 1);
     }
     // b) scores; c) mask
     f32x16 scur[C::KBLK];
@@ -348,23 +343,20 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
         pf[kb][j] = __builtin_bit_cast(bf16x8, w);
       }
     l_run += lsum;
-    // f) O^T += V^T P^T from V^T buffer PAR
+    // f) O^T += V^T P^T from V buffer PAR (P.V step 2kb + j covers keys 32kb + 16j ..)
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int d = 0; d < C::DBLK; ++d) {
-          const bf16x8 va = lds_load<bf16x8>(
-              lds + C::VT0 + PAR * C::TILE + d * 32 * C::VTROWB, vro[2 * kb + j]);
+          const lds_u8* vb = lds + C::VT0 + PAR * C::TILE + vtr[d] + (32 * kb + 16 * j) * C::ROWB;
+          const bf16x8 va = join_tr16(lds_tr16(vb), lds_tr16(vb + 4 * C::ROWB));
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][j], oacc[d], 0, 0, 0);
         }
-    // g) V(t+1) into V^T buffer PAR^1; the next tile must be in LDS before any wave
-    //    goes on (with key groups the caller holds the barrier, met by every group)
-    if (!LAST) {
-      store_v(PAR ^ 1);
-      if (KS == 1) __syncthreads();
-    }
+    // g) the next tile must be in LDS before any wave goes on (with key groups the
+    //    caller holds the barrier, met by every group)
+    if (!LAST && KS == 1) __syncthreads();
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -374,11 +366,10 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   if constexpr (KS == 1) {
     // ---- prologue: K(t_begin) and V(t_begin) in LDS ----
     if (n_tiles > t_begin) {
-      load_v(t_begin);
+      load_v(t_begin, 0);
       load_k(t_begin, 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): also drains the Q fragments
-    if (n_tiles > t_begin) store_v(0);
     __syncthreads();
     int t = t_begin;
     // tiles every row of the workgroup sees whole: no mask code at all
@@ -402,11 +393,10 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     const int my_first = t_begin + kgrp;
     const int n_steps = (n_tiles - t_begin + KS - 1) / KS;
     if (my_first < n_tiles) {
-      load_v(my_first);
+      load_v(my_first, 0);
       load_k(my_first, 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (my_first < n_tiles) store_v(0);
     __syncthreads();
     auto step = [&](int i, auto par_tag) {
       const int t = my_first + KS * i;
