@@ -18,25 +18,29 @@
 // swizzled K and V^T tiles) and the lazy online correction are described in
 // attn_bf16_tiles.hpp.
 //
-// Data movement.  K tiles go from global memory straight into LDS (buffer_load ...
-// lds, no staging registers), row-major; V tiles pass through registers and are
-// written transposed ([D][64 keys]).  Both are double buffered: the loads of tile
-// t+1 are issued before tile t is computed.  In both layouts the 16-byte chunks of a
-// row are XOR-swizzled with a function of the row, so the fragment reads are
-// bank-conflict free (the lanes the LDS serves together touch each bank once).  The
-// key loop is unrolled by two, so the buffer of every LDS access is known at compile
-// time and every fragment address is a per-lane register computed once plus an
-// immediate offset: no address arithmetic in the loop.
+// Data movement.  K and V tiles go from global memory straight into LDS
+// (buffer_load ... lds, no staging registers), row-major, double buffered: the loads
+// of tile t+1 are issued before tile t is computed.  The P.V operand (one dimension,
+// eight keys per lane) is read from the row-major V tile with transposing
+// ds_read_b64_tr_b16 reads, two per fragment.  The 16-byte chunks of each row are
+// XOR-swizzled with a function of the row (K and V each their own), so the fragment
+// reads are bank-conflict free (the lanes the LDS serves together touch each bank
+// once).  The key loop is unrolled by two, so the buffer of every LDS access is known
+// at compile time and every fragment address is a per-lane register computed once
+// plus an immediate offset: no address arithmetic in the loop.  (V used to pass
+// through registers and be written transposed with byte permutes: 16 vector
+// instructions per tile and thread, which the D = 64 tiles, bound by vector work,
+// paid for: the transposing reads gained 5-9 % there, same bits.)
 //
 // Key tile t:
-//   a) issue the loads of K(t+1) (LDS) and V(t+1) (registers)
+//   a) issue the loads of K(t+1) and V(t+1) (LDS)
 //   b) S(t) = K(t) Q^T on the matrix cores
 //   c) mask S(t) if the tile reaches past kv_len or crosses the causal diagonal
 //   d) row maxima -> exponent reference m(t); if a reference moved, O and l are
 //      multiplied by alpha(t) (rare, see attn_bf16_tiles.hpp)
 //   e) P(t) = exp2(S(t)*c - m(t)), its row sums and its bf16 packing
 //   f) O^T += V(t)^T P(t)^T on the matrix cores
-//   g) write V(t+1) transposed; barrier
+//   g) barrier (K(t+1) and V(t+1) have landed)
 // The two workgroups on a CU interleave these phases, so one wave's exponentials
 // run while the other's matrix instructions do.
 //
