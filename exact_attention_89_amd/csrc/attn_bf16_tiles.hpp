@@ -14,8 +14,10 @@
 // P.V step are consecutive, and so is the matching V^T operand (one dimension, 8
 // consecutive keys), a single 16-byte read from a transposed V tile.
 //
-// K tiles are stored row-major in LDS, V tiles transposed ([D][64 keys]); in both
-// the 16-byte chunks of a row are XOR-swizzled with a function of the row, so every
+// K tiles are stored row-major in LDS.  V tiles are stored transposed ([D][64 keys])
+// by the ping-pong kernel, and row-major by the four-wave kernel, which reads its P.V
+// operands with the transposing ds_read_b64_tr_b16 (lds_tr16).  In every layout the
+// 16-byte chunks of a row are XOR-swizzled with a function of the row, so every
 // fragment read is bank-conflict free (the lanes the LDS serves together touch each
 // bank once).
 #pragma once
