@@ -12,14 +12,17 @@
 // swap_bits23(i) (bits 2 and 3 exchanged), so register r of lane l holds key
 // 16*(r/8) + 8*(l/32) + r%8 of its 32-key block: the 8 keys a lane contributes to one
 // P.V step are consecutive, and so is the matching V^T operand (one dimension, 8
-// consecutive keys), a single 16-byte read from a transposed V tile.
+// consecutive keys).
 //
-// K tiles are stored row-major in LDS.  V tiles are stored transposed ([D][64 keys])
-// by the ping-pong kernel, and row-major by the four-wave kernel, which reads its P.V
-// operands with the transposing ds_read_b64_tr_b16 (lds_tr16).  In every layout the
-// 16-byte chunks of a row are XOR-swizzled with a function of the row, so every
-// fragment read is bank-conflict free (the lanes the LDS serves together touch each
-// bank once).
+// K and V tiles are stored row-major in LDS.  K fragments are single 16-byte reads; the
+// V^T operand is gathered from the row-major V tile by two transposing
+// ds_read_b64_tr_b16 (lds_tr16).  In both layouts the 16-byte chunks of a row are
+// XOR-swizzled with a function of the row, so every fragment read is bank-conflict free
+// (the lanes the LDS serves together touch each bank once).
+//
+// A transposing read is issued by the compiler only after every outstanding load of
+// the wave has landed when it cannot tell the read's LDS object from that of a pending
+// LDS DMA; the kernels therefore keep each V buffer in a __shared__ array of its own.
 #pragma once
 
 #include "common.hpp"
@@ -53,10 +56,6 @@ __device__ __forceinline__ int kswz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 
-// V^T rows are 64 keys (128 bytes, 8 chunks): two consecutive rows span the banks.
-// Adding 32 to the row leaves it unchanged.
-__device__ __forceinline__ int vtswz(int d) { return (d >> 1) & 7; }
-
 // v_permlane32_swap exchanges the upper half-wave of one operand with the lower
 // half-wave of the other; with both operands = x, the two results of every lane are
 // x[l] and x[l ^ 32] (in some order), so their max / sum is the two-lane reduction.
@@ -76,7 +75,7 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Swizzle of the 16-byte chunks of a row-major V tile (4-wave kernel): row bits 0-1
+// Swizzle of the 16-byte chunks of a row-major V tile: row bits 0-1
 // select the 64-byte window, so a transposing read that gathers four consecutive keys
 // touches four windows; it does not change when the row moves by a multiple of 4.
 template <int D>

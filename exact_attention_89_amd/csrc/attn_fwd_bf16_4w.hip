@@ -15,14 +15,16 @@
 // workgroups (two waves per SIMD) share a CU and hide each other's latencies.
 //
 // Register and LDS layouts (transposed scores, P straight from the score registers,
-// swizzled K and V^T tiles) and the lazy online correction are described in
+// swizzled K and V tiles) and the lazy online correction are described in
 // attn_bf16_tiles.hpp.
 //
 // Data movement.  K and V tiles go from global memory straight into LDS
 // (buffer_load ... lds, no staging registers), row-major, double buffered: the loads
 // of tile t+1 are issued before tile t is computed.  The P.V operand (one dimension,
 // eight keys per lane) is read from the row-major V tile with transposing
-// ds_read_b64_tr_b16 reads, two per fragment.  The 16-byte chunks of each row are
+// ds_read_b64_tr_b16 reads, two per fragment (each V buffer is an LDS array of its
+// own, so these reads need not wait for the next tile's loads).  The 16-byte chunks of
+// each row are
 // XOR-swizzled with a function of the row (K and V each their own), so the fragment
 // reads are bank-conflict free (the lanes the LDS serves together touch each bank
 // once).  The key loop is unrolled by two, so the buffer of every LDS access is known
@@ -58,13 +60,12 @@ struct Cfg {
   static constexpr int BC = 64;                  // keys per tile
   static constexpr int NT = 64 * RW;             // threads per key group
   static constexpr int ROWB = D * 2;             // bytes per K row
-  static constexpr int TILE = BC * ROWB;         // bytes per K tile (and per V^T tile)
+  static constexpr int TILE = BC * ROWB;         // bytes per K (or V) tile
   static constexpr int DMA = TILE / 1024 / RW;   // 1 KiB K loads per wave per tile
   static constexpr int DSTEPS = D / 16;          // k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
   static constexpr int KBLK = BC / 32;           // 32-key blocks of a tile
-  static constexpr int LDS = 4 * TILE;           // K double buffer, V^T double buffer
-  static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
+  static constexpr int OX = DBLK * 16 * NT * 4;  // bytes of one key group's O (fp32)
   static_assert((BC / 4) * (D / 8) <= NT || NT == 256, "V staging: one unit a thread");
 };
 
@@ -78,7 +79,7 @@ struct Cfg {
 // KS, RW: key groups per workgroup and row waves per group.  The plain kernel is
 // KS = 1, RW = 4 (four waves, 128 rows).  With KS > 1 the workgroup has KS groups of
 // RW waves; every group covers the same 32*RW query rows, group g takes the key tiles
-// t = g, g + KS, ... (each group with its own K / V^T double buffers), and at the end
+// t = g, g + KS, ... (each group with its own K / V double buffers), and at the end
 // groups 1 .. KS-1 hand their (O, m, l) to group 0 through LDS, where they are combined
 // with the same rescaling as any reference move.  For grids too small to fill the GPU:
 // KS = 2, RW = 4 halves the sequential key loop of a 128-row block (D = 128); KS = 2,
@@ -92,14 +93,32 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   static_assert(RW == 4 || KS > 1, "fewer row waves only with key groups");
   static_assert(KS * RW <= 8, "at most 8 waves a workgroup");
   using C = Cfg<D, RW>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS * KS];
+  // Each of the four tile buffers (K and V, double buffered; one slot per key group)
+  // is an LDS array of its own: a fragment read of one buffer while a DMA into the
+  // other is in flight must not look like a possible overlap to the compiler, which
+  // would wait for the outstanding loads first (see attn_bf16_tiles.hpp).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_k0[C::TILE * KS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_k1[C::TILE * KS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_v0[C::TILE * KS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_v1[C::TILE * KS];
+  static_assert(KS <= 2, "the O exchange below is written for two key groups");
+  static_assert(KS == 1 || C::OX / 2 <= C::TILE * KS, "half of a key group's O fits a K buffer");
+  static_assert(KS == 1 || 3 * C::NT * 4 <= C::TILE * KS, "row statistics fit a V buffer");
   const int tid = threadIdx.x;
   // wave-uniform values in scalar registers (branches on them must be real branches:
   // every wave meets every barrier)
   const int wave = KS == 1 ? (tid >> 6) : (__builtin_amdgcn_readfirstlane(tid >> 6) % RW);
   const int kgrp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / RW;   // key group
   const int tid_g = tid % C::NT;                   // thread inside its key group
-  lds_u8* const lds = (lds_u8*)smem + kgrp * C::LDS;
+  // buffer `buf` of a tile array; this key group's slot starts goff bytes in (added to
+  // the DMA targets and folded into the per-lane fragment offsets)
+  auto kbuf = [&](int buf) __attribute__((always_inline)) {
+    return buf ? (lds_u8*)smem_k1 : (lds_u8*)smem_k0;
+  };
+  auto vbuf = [&](int buf) __attribute__((always_inline)) {
+    return buf ? (lds_u8*)smem_v1 : (lds_u8*)smem_v0;
+  };
+  const unsigned goff = (unsigned)kgrp * C::TILE;
   const int lane = tid & 63;
   const int lq = lane & 31;   // query column inside the wave's 32 rows
   const int lg = lane >> 5;   // half of the wave
@@ -200,7 +219,7 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   auto load_k = [&](int t, int stage) {
 #pragma unroll
     for (int n = 0; n < C::DMA; ++n)
-      buffer_load16_to_lds(krs, (lds_void*)(lds + stage * C::TILE + (wave * C::DMA + n) * 1024),
+      buffer_load16_to_lds(krs, (lds_void*)(kbuf(stage) + goff + (wave * C::DMA + n) * 1024),
                            koff[n], t * C::BC * ld * 2);
   };
 
@@ -227,7 +246,7 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
 #pragma unroll
     for (int n = 0; n < C::DMA; ++n)
       buffer_load16_to_lds(vrs,
-                           (lds_void*)(lds + C::VT0 + stage * C::TILE + (wave * C::DMA + n) * 1024),
+                           (lds_void*)(vbuf(stage) + goff + (wave * C::DMA + n) * 1024),
                            voff[n], t * C::BC * ld * 2);
   };
   unsigned vtr[C::DBLK];   // read q of 32-dimension block d at P.V step s: + (16 s + 4 q) rows
@@ -236,7 +255,7 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     const int key = 8 * (gg >> 1) + m;
 #pragma unroll
     for (int d = 0; d < C::DBLK; ++d)
-      vtr[d] = key * C::ROWB + (((4 * d + 2 * (gg & 1) + (a >> 1)) ^ vswz<D>(key)) * 16) +
+      vtr[d] = goff + key * C::ROWB + (((4 * d + 2 * (gg & 1) + (a >> 1)) ^ vswz<D>(key)) * 16) +
                8 * (a & 1);
   }
 
@@ -245,7 +264,7 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   unsigned kro[C::DSTEPS];
 #pragma unroll
   for (int s = 0; s < C::DSTEPS; ++s)
-    kro[s] = krow * C::ROWB + (((2 * s + lg) ^ kswz<D>(krow)) * 16);
+    kro[s] = goff + krow * C::ROWB + (((2 * s + lg) ^ kswz<D>(krow)) * 16);
 
   // S^T = K Q^T for the tile in K buffer `stage`, fp32 accumulation from 0
   auto qk = [&](int stage, f32x16* sacc) {
@@ -254,7 +273,7 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
 #pragma unroll
       for (int kb = 0; kb < C::KBLK; ++kb) {
         const bf16x8 a =
-            lds_load<bf16x8>(lds + stage * C::TILE + kb * 32 * C::ROWB, kro[s]);
+            lds_load<bf16x8>(kbuf(stage) + kb * 32 * C::ROWB, kro[s]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             a, qf[s], s == 0 ? (f32x16){} : sacc[kb], 0, 0, 0);
       }
@@ -354,13 +373,16 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int d = 0; d < C::DBLK; ++d) {
-          const lds_u8* vb = lds + C::VT0 + PAR * C::TILE + vtr[d] + (32 * kb + 16 * j) * C::ROWB;
+          const lds_u8* vb = vbuf(PAR) + vtr[d] + (32 * kb + 16 * j) * C::ROWB;
           const bf16x8 va = join_tr16(lds_tr16(vb), lds_tr16(vb + 4 * C::ROWB));
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][j], oacc[d], 0, 0, 0);
         }
     // g) the next tile must be in LDS before any wave goes on (with key groups the
     //    caller holds the barrier, met by every group)
-    if (!LAST && KS == 1) __syncthreads();
+    if (!LAST && KS == 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's K(t+1), V(t+1) landed
+      __syncthreads();
+    }
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -409,24 +431,31 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
         if (t + KS < n_tiles) iteration(t, par_tag, F_{}, T_{}, KS);
         else iteration(t, par_tag, T_{}, T_{}, KS);
       }
-      if (more) __syncthreads();
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+      }
     };
     for (int i = 0; i < n_steps; i += 2) {
       step(i, I0{});
       if (i + 1 < n_steps) step(i + 1, I1{});
     }
-    // hand the (O, m, l) of groups 1 .. KS-1 to group 0: each group's own LDS region
-    // takes its O, group 0's region the row statistics (every region is free once all
-    // groups have left the loop)
+    // hand the (O, m, l) of group 1 to group 0: the K buffers take its O (the first
+    // half of the 32-dimension blocks in one, the rest in the other), the first V
+    // buffers the row statistics (all buffers are free once every group has left the
+    // loop)
     __syncthreads();
-    float* s_x = (float*)smem;
+    float* s_x = (float*)smem_v0;
+    auto o_x = [&](int d) __attribute__((always_inline)) {
+      constexpr int HB = C::DBLK / 2;
+      return (float*)(d < HB ? (lds_u8*)smem_k0 : (lds_u8*)smem_k1) + (d % HB) * 16 * C::NT;
+    };
     const int slot = wave * 64 + lane;             // < 64 * RW
     if (kgrp > 0) {
-      float* o_x = (float*)((lds_u8*)smem + kgrp * C::LDS);
 #pragma unroll
       for (int d = 0; d < C::DBLK; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o_x[(d * 16 + r) * C::NT + slot] = oacc[d][r];
+        for (int r = 0; r < 16; ++r) o_x(d)[r * C::NT + slot] = oacc[d][r];
       float* st = s_x + (kgrp - 1) * 3 * C::NT;
       st[slot] = m_run;
       st[C::NT + slot] = m_use;
@@ -452,11 +481,10 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
         const float mg = st[slot], mug = st[C::NT + slot], lg_ = st[2 * C::NT + slot];
         const float fg = mg == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mug - M);
         l_run += lg_ * fg;
-        const float* o_x = (const float*)((lds_u8*)smem + g * C::LDS);
 #pragma unroll
         for (int d = 0; d < C::DBLK; ++d)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[d][r] += o_x[(d * 16 + r) * C::NT + slot] * fg;
+          for (int r = 0; r < 16; ++r) oacc[d][r] += o_x(d)[r * C::NT + slot] * fg;
       }
       m_run = M;
       m_use = M;
@@ -531,7 +559,7 @@ int launch_attn_fwd_bf16_4w(const FwdArgs& a, int D, hipStream_t stream, int key
   if (key_groups == 2) {
     // D = 64: 64-row blocks, two key groups of two row waves (4 waves, two workgroups
     // per CU); D = 128: 128-row blocks, two key groups of four row waves (each group's
-    // K / V^T buffers take 64 KiB of LDS, one workgroup per CU)
+    // K / V buffers take 64 KiB of LDS, one workgroup per CU)
     if (D == 64) return launch_4w<false, false, 2, 2>(a, D, stream);
     return launch_4w<false, false, 2, 4>(a, D, stream);
   }

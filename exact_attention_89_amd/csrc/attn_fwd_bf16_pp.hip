@@ -26,7 +26,7 @@
 //   ...     (every phase ends with a workgroup barrier)
 //
 // Register and LDS layouts (transposed scores, P straight from the score registers,
-// swizzled K and V^T tiles) and the lazy online correction are described in
+// swizzled K and V tiles) and the lazy online correction are described in
 // attn_bf16_tiles.hpp.
 //
 // Masking.  The leading key tiles that every row of the workgroup sees whole run a
@@ -38,14 +38,17 @@
 // the key-length tail) skips that tile's products and softmax, whose contributions
 // would be exact zeros; it still moves data and meets every barrier.
 //
-// Data movement.  G1 moves K tiles from global memory straight into LDS
-// (buffer_load ... lds, no staging registers), row-major; G0 loads V tiles into
-// registers and writes them transposed ([D][64 keys]) during its softmax phase.
-// Both are double buffered and requested two phases before first use.  In both
-// layouts the 16-byte chunks of a row are XOR-swizzled with a function of the row,
-// so the fragment reads are bank-conflict free.  Buffer indices are compile-time
-// constants (the loop is unrolled by two), so every fragment address is a per-lane
-// register computed once plus an immediate offset.
+// Data movement.  Both tiles go from global memory straight into LDS (buffer_load
+// ... lds, no staging registers), row-major, double buffered: G1 requests K(t+2) at
+// the start of its softmax phase of tile t, G0 requests V(t) at the start of its
+// matrix phase of tile t (the first phase after the last read of that buffer), and
+// each waits for its own loads before the barrier that publishes them.  The 16-byte
+// chunks of a row are XOR-swizzled with a function of the row (kswz for K, vswz for
+// V), so the fragment reads are bank-conflict free: K fragments by ds_read_b128, the
+// P.V operand (8 consecutive keys of one dimension) by two transposing
+// ds_read_b64_tr_b16.  Buffer indices are compile-time constants (the loop is
+// unrolled by two), so every fragment address is a per-lane register computed once
+// plus an immediate offset.
 
 #include <type_traits>
 
@@ -63,16 +66,11 @@ struct Cfg {
   static constexpr int BC = 64;                  // keys per tile
   static constexpr int NT = 512;                 // threads per workgroup (8 waves)
   static constexpr int ROWB = D * 2;             // bytes per K row
-  static constexpr int TILE = BC * ROWB;         // bytes per K tile (and per V^T tile)
-  static constexpr int VTROWB = BC * 2;          // bytes per V^T row (64 keys)
-  static constexpr int KDMA = TILE / 1024 / 4;   // 1 KiB K loads per G1 wave per tile
-  static constexpr int V_UNITS = (BC / 4) * (D / 8);  // G0 threads staging V (4 keys x 8 dims)
+  static constexpr int TILE = BC * ROWB;         // bytes per K (or V) tile
+  static constexpr int KDMA = TILE / 1024 / 4;   // 1 KiB loads per wave per tile
   static constexpr int DSTEPS = D / 16;          // k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
   static constexpr int KBLK = BC / 32;           // 32-key blocks of a tile
-  static constexpr int LDS = 4 * TILE;           // K double buffer, V^T double buffer
-  static constexpr int VT0 = 2 * TILE;           // offset of the V^T buffers
-  static_assert(V_UNITS <= 256, "V staging must fit in group 0");
 };
 
 // Phase boundary: this wave's LDS accesses are complete, then all 8 waves meet.
@@ -101,6 +99,24 @@ __device__ __forceinline__ void schedule_mfma_phase() {
   __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
 }
 
+// The same for MFMAs that take two fragment reads each (P.V operands gathered by
+// transposing reads), optionally followed by NQ MFMAs with one read each (Q.K^T).
+template <int NPV, int NQ>
+__device__ __forceinline__ void schedule_mfma_phase_pv() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPrefetch, 0);
+#pragma unroll
+  for (int i = 0; i < NPV - kPrefetch; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
+}
+
 // The wave in its MFMA phase gets issue priority over its SIMD partner (which is in
 // its softmax phase), so the matrix core is refilled as soon as it frees up.
 __device__ __forceinline__ void mfma_priority() { __builtin_amdgcn_s_setprio(1); }
@@ -111,8 +127,17 @@ __device__ __forceinline__ void valu_priority() { __builtin_amdgcn_s_setprio(0);
 template <int D, bool PRE>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
-  lds_u8* const lds = (lds_u8*)smem;
+  // K double buffer; the two V buffers are arrays of their own, so the compiler can
+  // tell that a transposing read of one V buffer does not touch the other one while a
+  // DMA into it is in flight (for reads it cannot separate from a pending DMA target
+  // it waits for every outstanding load first)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_k[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_v0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_v1[C::TILE];
+  lds_u8* const lds = (lds_u8*)smem_k;
+  auto vbuf = [&](int buf) __attribute__((always_inline)) {
+    return buf ? (lds_u8*)smem_v1 : (lds_u8*)smem_v0;
+  };
 
   const int tid = threadIdx.x;
   // wave-uniform values live in scalar registers, so branches on them are real
@@ -191,40 +216,39 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
                            koff[n], t * C::BC * D * 2);
   };
 
-  // ---- V (G0): global -> registers -> LDS, transposed ----
-  // Thread (kg, dg) holds keys 4kg..4kg+3 x dimensions 8dg..8dg+7 (four 16-byte
-  // loads) and writes them as 8 rows of V^T, 4 keys (8 bytes) each.
+  // ---- V (G0): global -> LDS without registers, row-major ----
+  // Same movement as K, with the V swizzle vswz (row bits 0-1 pick the 64-byte window).
+  // The P.V operand (one dimension per lane, the 8 keys of its P fragment) is read back
+  // with the transposing ds_read_b64_tr_b16 (see lds_tr16): the lane at position
+  // i = 4m + a of a group of 16 lanes (group g) addresses, in read q, key
+  // 8(g/2) + 4q + m (plus the P.V step's 16-key offset) at dimensions
+  // 16(g%2) + 4a .. + 4 of the 32-dimension block, so two reads give a lane its 8
+  // elements; the four keys one read gathers fall in four different 64-byte windows.
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (unsigned)L * D * 2);
-  const bool v_owner = C::V_UNITS >= 256 || tid < C::V_UNITS;   // used by G0 only
-  const int vkg = tid % (C::BC / 4), vdg = (tid / (C::BC / 4)) % (D / 8);
-  const unsigned vgoff = ((unsigned)(4 * vkg) * D + 8 * vdg) * 2;
-  unsigned vwoff[4];  // V^T byte offset of row 8dg + 2x (row 8dg + 2x + 1: + VTROWB)
+  unsigned voff[C::KDMA];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int d = 8 * vdg + 2 * x;
-    vwoff[x] = d * C::VTROWB + (((vkg >> 1) ^ vtswz(d)) * 16) + (vkg & 1) * 8;
+  for (int n = 0; n < C::KDMA; ++n) {
+    const int byte = (wg * C::KDMA + n) * 1024 + 16 * lane;
+    const int row = byte / C::ROWB;
+    const int ch = ((byte % C::ROWB) / 16) ^ vswz<D>(row);
+    voff[n] = ((unsigned)row * D + 8 * ch) * 2;
   }
-  u32x4 vreg[4];
-  auto load_v = [&](int t) __attribute__((always_inline)) {
-    if (v_owner) {
+  auto load_v = [&](int t, int stage) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = buffer_load16_so(vrs, vgoff + r * D * 2, t * C::BC * D * 2);
-    }
+    for (int n = 0; n < C::KDMA; ++n)
+      buffer_load16_to_lds(vrs,
+                           (lds_void*)(vbuf(stage) + (wg * C::KDMA + n) * 1024),
+                           voff[n], t * C::BC * D * 2);
   };
-  auto store_v = [&](int buf) __attribute__((always_inline)) {
-    if (v_owner) {
+  unsigned vtr[C::DBLK];   // read q of 32-dimension block d at P.V step s: + (16 s + 4 q) rows
+  {
+    const int gi = lane & 15, gg = lane >> 4, a = gi & 3, m = gi >> 2;
+    const int key = 8 * (gg >> 1) + m;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // row 8dg + e of V^T: dimension e of keys 4kg .. 4kg + 3
-        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const u32x2 pk = {__builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel),
-                          __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel)};
-        *(__attribute__((address_space(3))) u32x2*)(
-            lds + C::VT0 + buf * C::TILE + vwoff[e >> 1] + (e & 1) * C::VTROWB) = pk;
-      }
-    }
-  };
+    for (int d = 0; d < C::DBLK; ++d)
+      vtr[d] = key * C::ROWB + (((4 * d + 2 * (gg & 1) + (a >> 1)) ^ vswz<D>(key)) * 16) +
+               8 * (a & 1);
+  }
 
   // ---- fragment read offsets (per lane, fixed for the whole loop) ----
   const int krow = swap_bits23(lq);   // key (row of K) this lane feeds to the MFMA
@@ -232,10 +256,6 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
 #pragma unroll
   for (int s = 0; s < C::DSTEPS; ++s)
     kro[s] = krow * C::ROWB + (((2 * s + lg) ^ kswz<D>(krow)) * 16);
-  unsigned vro[C::KBLK * 2];
-#pragma unroll
-  for (int x = 0; x < C::KBLK * 2; ++x)
-    vro[x] = lq * C::VTROWB + (((2 * x + lg) ^ vtswz(lq)) * 16);
 
   // ---- running state: one query per lane (shared by lanes l and l^32) ----
   f32x16 oacc[C::DBLK];
@@ -261,7 +281,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
             a, qf[s], s == 0 ? (f32x16){} : sacc[kb], 0, 0, 0);
       }
   };
-  // O^T += V^T P^T from V^T buffer `buf`
+  // O^T += V^T P^T from V buffer `buf`
   auto pv = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
@@ -269,8 +289,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int d = 0; d < C::DBLK; ++d) {
-          const bf16x8 va = lds_load<bf16x8>(
-              lds + C::VT0 + buf * C::TILE + d * 32 * C::VTROWB, vro[2 * kb + j]);
+          const lds_u8* vb = vbuf(buf) + vtr[d] + (32 * kb + 16 * j) * C::ROWB;
+          const bf16x8 va = join_tr16(lds_tr16(vb), lds_tr16(vb + 4 * C::ROWB));
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][j], oacc[d], 0, 0, 0);
         }
   };
@@ -362,9 +382,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   };
 
   // One tile period of group G; PAR = t & 1 selects the buffers at compile time.
-  //   MFMA phase:    O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
-  //   softmax phase: G0 writes V(t) to V^T buffer PAR and requests V(t+1), G1
-  //                  requests K(t+2) into K buffer PAR; then P(t)
+  //   MFMA phase:    G0 requests V(t) into V buffer PAR (last read by G1's P.V(t-2),
+  //                  one phase earlier); O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
+  //   softmax phase: G1 requests K(t+2) into K buffer PAR; P(t); G0 waits for V(t),
+  //                  which both groups read from the next phase on
   auto period = [&](const int t, auto grp_tag, auto par_tag, auto first_tag, auto mask_tag)
                     __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
@@ -372,35 +393,39 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     constexpr bool FIRST = decltype(first_tag)::value;
     constexpr bool MASKED = decltype(mask_tag)::value;
     mfma_priority();
+    if (G == 0) {
+      load_v(t, PAR);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int NPV = C::KBLK * 2 * C::DBLK, NQK = C::DSTEPS * C::KBLK;
     if (MASKED) {
       // boundary tiles: a tile none of whose keys this wave's rows see adds exact
       // zeros to O and l, so its products and softmax are skipped (loads and
       // barriers still run: the other waves need the tiles)
       if (!FIRST && !wave_blind(t - 1)) {
         pv(PAR ^ 1);
-        schedule_mfma_phase<C::DSTEPS * C::KBLK>();
+        schedule_mfma_phase_pv<NPV, 0>();
       }
       if (!wave_blind(t)) {
         qk(PAR);
         schedule_mfma_phase<C::DSTEPS * C::KBLK>();
       }
     } else {
-      if (!FIRST) pv(PAR ^ 1);
-      qk(PAR);
-      schedule_mfma_phase<FIRST ? C::DSTEPS * C::KBLK : 2 * C::DSTEPS * C::KBLK>();
+      if (!FIRST) {
+        pv(PAR ^ 1);
+        qk(PAR);
+        schedule_mfma_phase_pv<NPV, NQK>();
+      } else {
+        qk(PAR);
+        schedule_mfma_phase<NQK>();
+      }
     }
     if (G == 1) wait_vm0();   // K(t+1) has landed: it is read after the barrier
     phase_barrier();
     valu_priority();
-    // data movement first: the V^T writes then drain while the exponentials run
-    // instead of at the barrier (V^T buffer PAR was last read by P.V(t-2))
-    if (G == 0) {
-      store_v(PAR);
-      if (t + 1 < n_tiles) load_v(t + 1);
-    } else {
-      if (t + 2 < n_tiles) load_k(t + 2, PAR);
-    }
+    if (G == 1 && t + 2 < n_tiles) load_k(t + 2, PAR);
     if (!MASKED || !wave_blind(t)) softmax(t, mask_tag);
+    if (G == 0) wait_vm0();   // V(t) has landed: it is read after the barrier
     phase_barrier();
   };
 
@@ -411,11 +436,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     constexpr int G = decltype(grp_tag)::value;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // prologue: K(0) in LDS, V(0) on its way
-    if (n_tiles > 0) {
-      if (G == 1) load_k(0, 0);
-      else load_v(0);
-    }
+    // prologue: K(0) in LDS (V(0) is requested in the first period)
+    if (n_tiles > 0 && G == 1) load_k(0, 0);
     if (G == 1) wait_vm0();
     phase_barrier();
     if (n_tiles > 0) {

@@ -36,9 +36,11 @@
 // Data movement.  K and V tiles both go global -> LDS by buffer_load ... lds
 // (row-major, 16-byte chunks XOR-swizzled by row), double buffered, no registers and
 // no vector instructions; the key loop is unrolled by two so every LDS offset is an
-// immediate.  (Staging V through registers and transposing it with byte permutes cost
-// 16 vector instructions per tile and thread, in a kernel whose vector unit is the
-// bottleneck; the transposing reads replaced them: +8 % at B=1 H=32 N=8192 causal.)
+// immediate, and each buffer is an LDS array of its own so that no fragment read waits
+// for the next tile's loads.  (Staging V through registers and transposing it with
+// byte permutes cost 16 vector instructions per tile and thread, in a kernel whose
+// vector unit is the bottleneck; the transposing reads replaced them: +8 % at B=1
+// H=32 N=8192 causal.)
 #include <type_traits>
 
 #include "attn_fp8_tiles.hpp"
@@ -53,20 +55,29 @@ struct Cfg8 {
   static constexpr int BC = 64;                  // keys per tile
   static constexpr int NT = 256;                 // threads per workgroup
   static constexpr int ROWB = D;                 // bytes per K row
-  static constexpr int TILE = BC * D;            // bytes per K tile (and per V^T tile)
+  static constexpr int TILE = BC * D;            // bytes per K (or V) tile
   static constexpr int DMA = TILE / 1024 / 4;    // 1 KiB K loads per wave per tile
   static constexpr int DSTEPS = D / 64;          // k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 32;            // 32-dimension blocks of O^T
-  static constexpr int LDS = 4 * TILE;           // K double buffer, V double buffer
-  static constexpr int VT0 = 2 * TILE;           // offset of the V buffers
 };
 
 // PRE: scale <= 0, scores are scaled before they are masked.
 template <int D, bool PRE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v_descale) {
   using C = Cfg8<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
-  lds_u8* const lds = (lds_u8*)smem;
+  // K and V double buffers, each buffer an LDS array of its own: a fragment read of one
+  // buffer while a DMA into the other is in flight must not look like a possible
+  // overlap to the compiler, which would wait for the outstanding loads first
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_k0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_k1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_v0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_v1[C::TILE];
+  auto kbuf = [&](int buf) __attribute__((always_inline)) {
+    return buf ? (lds_u8*)smem_k1 : (lds_u8*)smem_k0;
+  };
+  auto vbuf = [&](int buf) __attribute__((always_inline)) {
+    return buf ? (lds_u8*)smem_v1 : (lds_u8*)smem_v0;
+  };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
   auto load_k = [&](int t, int stage) {
 #pragma unroll
     for (int n = 0; n < C::DMA; ++n)
-      buffer_load16_to_lds(krs, (lds_void*)(lds + stage * C::TILE + (wave * C::DMA + n) * 1024),
+      buffer_load16_to_lds(krs, (lds_void*)(kbuf(stage) + (wave * C::DMA + n) * 1024),
                            koff[n], t * C::BC * D);
   };
 
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
 #pragma unroll
     for (int n = 0; n < C::DMA; ++n)
       buffer_load16_to_lds(vrs,
-                           (lds_void*)(lds + C::VT0 + stage * C::TILE + (wave * C::DMA + n) * 1024),
+                           (lds_void*)(vbuf(stage) + (wave * C::DMA + n) * 1024),
                            koff[n], t * C::BC * D);
   };
   unsigned vtr[C::DBLK];   // read q of 32-dimension block d: vtr[d] + 16 q rows
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     for (int s = 0; s < C::DSTEPS; ++s)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const lds_u8* base = lds + stage * C::TILE + kb * 32 * C::ROWB;
+        const lds_u8* base = kbuf(stage) + kb * 32 * C::ROWB;
         const i32x8 a = join32(lds_load<u32x4>(base, kro[s][0]), lds_load<u32x4>(base, kro[s][1]));
         sacc[kb] = mfma_fp8(a, qf[s], s == 0 ? (f32x16){} : sacc[kb]);
       }
@@ -246,12 +257,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     // O^T += V^T P^T
 #pragma unroll
     for (int d = 0; d < C::DBLK; ++d) {
-      const lds_u8* base = lds + C::VT0 + PAR * C::TILE + vtr[d];
+      const lds_u8* base = vbuf(PAR) + vtr[d];
       const i32x8 va = join_tr8(lds_tr8(base), lds_tr8(base + 16 * C::ROWB),
                                 lds_tr8(base + 32 * C::ROWB), lds_tr8(base + 48 * C::ROWB));
       oacc[d] = mfma_fp8(va, pf, oacc[d]);
     }
-    if (!LAST) __syncthreads();
+    if (!LAST) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's K(t+1), V(t+1) landed
+      __syncthreads();
+    }
   };
 
   if (n_tiles > 0) {
