@@ -19,7 +19,7 @@
 // vector work of the other group hides behind it.
 //
 //   phase   G0                          G1
-//   0       S(0) = K(0) Q^T             (loads K(1))
+//   0       S(0) = K(0) Q^T             -
 //   1       softmax(0) -> P(0)          S(0)
 //   2       O += V(0) P(0); S(1)        softmax(0)
 //   3       softmax(1)                  O += V(0) P(0); S(1)
@@ -39,10 +39,13 @@
 // would be exact zeros; it still moves data and meets every barrier.
 //
 // Data movement.  Both tiles go from global memory straight into LDS (buffer_load
-// ... lds, no staging registers), row-major, double buffered: G1 requests K(t+2) at
-// the start of its softmax phase of tile t, G0 requests V(t) at the start of its
-// matrix phase of tile t (the first phase after the last read of that buffer), and
-// each waits for its own loads before the barrier that publishes them.  The 16-byte
+// ... lds, no staging registers), row-major, double buffered.  G0 moves all of it:
+// in its matrix phase of tile t (the first phase after the last reads of those
+// buffers) it requests V(t) and K(t+1), spread between its MFMAs, and it waits for
+// them at the end of its softmax phase, before the barrier that publishes them.  (A
+// wave whose request the memory pipeline cannot take yet stalls; in a matrix phase
+// the matrix core works through its queued MFMAs meanwhile, in a softmax phase the
+// exponentials would wait.)  The 16-byte
 // chunks of a row are XOR-swizzled with a function of the row (kswz for K, vswz for
 // V), so the fragment reads are bank-conflict free: K fragments by ds_read_b128, the
 // P.V operand (8 consecutive keys of one dimension) by two transposing
@@ -101,18 +104,23 @@ __device__ __forceinline__ void schedule_mfma_phase() {
 
 // The same for MFMAs that take two fragment reads each (P.V operands gathered by
 // transposing reads), optionally followed by NQ MFMAs with one read each (Q.K^T).
-template <int NPV, int NQ>
+// NVM global-memory requests (tile DMA) go one after every kVmStride MFMAs: the memory
+// pipeline accepts a CU's requests at a limited rate, and a wave whose request has to
+// wait stalls, which costs little while the matrix core still has queued MFMAs.
+constexpr int kVmStride = 2;
+template <int NPV, int NQ, int NVM = 0>
 __device__ __forceinline__ void schedule_mfma_phase_pv() {
+  static_assert(NVM <= (NPV + NQ - kPrefetch) / kVmStride, "room for every request");
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPrefetch, 0);
 #pragma unroll
-  for (int i = 0; i < NPV - kPrefetch; ++i) {
+  for (int i = 0; i < NPV + NQ - kPrefetch; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i < NPV - kPrefetch)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i % kVmStride == kVmStride - 1 && i / kVmStride < NVM)
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
 }
@@ -127,14 +135,17 @@ __device__ __forceinline__ void valu_priority() { __builtin_amdgcn_s_setprio(0);
 template <int D, bool PRE>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   using C = Cfg<D>;
-  // K double buffer; the two V buffers are arrays of their own, so the compiler can
-  // tell that a transposing read of one V buffer does not touch the other one while a
-  // DMA into it is in flight (for reads it cannot separate from a pending DMA target
-  // it waits for every outstanding load first)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_k[2 * C::TILE];
+  // K and V double buffers, each buffer an LDS array of its own, so the compiler can
+  // tell that a fragment read of one buffer does not touch another one while a DMA
+  // into it is in flight (for reads it cannot separate from a pending DMA target it
+  // waits for every outstanding load first)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_k0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_k1[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char smem_v0[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char smem_v1[C::TILE];
-  lds_u8* const lds = (lds_u8*)smem_k;
+  auto kbuf = [&](int buf) __attribute__((always_inline)) {
+    return buf ? (lds_u8*)smem_k1 : (lds_u8*)smem_k0;
+  };
   auto vbuf = [&](int buf) __attribute__((always_inline)) {
     return buf ? (lds_u8*)smem_v1 : (lds_u8*)smem_v0;
   };
@@ -196,11 +207,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     qf[s] = __builtin_bit_cast(bf16x8,
                                buffer_load16(qrs, ((unsigned)qrow * D + 16 * s + 8 * lg) * 2));
 
-  // ---- K (G1): global -> LDS without registers ----
-  // Load n of G1 wave wg writes tile bytes [m*1024, m*1024 + 1024), m = wg*KDMA + n,
+  // ---- K (G0): global -> LDS without registers ----
+  // Load n of G0 wave wg writes tile bytes [m*1024, m*1024 + 1024), m = wg*KDMA + n,
   // lane i the 16 bytes at m*1024 + 16*i; the lane fetches the global chunk the
   // swizzle puts there.  The tile start is the scalar offset of the load.
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)L * D * 2);
+  // Keys from kv_end on (which no row of the block sees) read as zeros, so the request
+  // for the tile past the last one fetches nothing.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)kv_end * D * 2);
   unsigned koff[C::KDMA];
 #pragma unroll
   for (int n = 0; n < C::KDMA; ++n) {
@@ -212,7 +225,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   auto load_k = [&](int t, int stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < C::KDMA; ++n)
-      buffer_load16_to_lds(krs, (lds_void*)(lds + stage * C::TILE + (wg * C::KDMA + n) * 1024),
+      buffer_load16_to_lds(krs, (lds_void*)(kbuf(stage) + (wg * C::KDMA + n) * 1024),
                            koff[n], t * C::BC * D * 2);
   };
 
@@ -276,7 +289,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
 #pragma unroll
       for (int kb = 0; kb < C::KBLK; ++kb) {
         const bf16x8 a =
-            lds_load<bf16x8>(lds + stage * C::TILE + kb * 32 * C::ROWB, kro[s]);
+            lds_load<bf16x8>(kbuf(stage) + kb * 32 * C::ROWB, kro[s]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             a, qf[s], s == 0 ? (f32x16){} : sacc[kb], 0, 0, 0);
       }
@@ -383,9 +396,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
 
   // One tile period of group G; PAR = t & 1 selects the buffers at compile time.
   //   MFMA phase:    G0 requests V(t) into V buffer PAR (last read by G1's P.V(t-2),
-  //                  one phase earlier); O += V(t-1) P(t-1) (t > 0), S(t) = K(t) Q^T
-  //   softmax phase: G1 requests K(t+2) into K buffer PAR; P(t); G0 waits for V(t),
-  //                  which both groups read from the next phase on
+  //                  one phase earlier) and K(t+1) into K buffer PAR ^ 1 (last read by
+  //                  G1's Q.K^T(t-1), one phase earlier); O += V(t-1) P(t-1) (t > 0),
+  //                  S(t) = K(t) Q^T
+  //   softmax phase: P(t); G0 waits for V(t) and K(t+1), which both groups read from
+  //                  the next phase on
+  // The requests go out between the MFMAs of an interior tile, and first otherwise
+  // (the products of a boundary tile may be skipped).  G1 moves no data.
   auto period = [&](const int t, auto grp_tag, auto par_tag, auto first_tag, auto mask_tag)
                     __attribute__((always_inline)) {
     constexpr int G = decltype(grp_tag)::value;
@@ -393,11 +410,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     constexpr bool FIRST = decltype(first_tag)::value;
     constexpr bool MASKED = decltype(mask_tag)::value;
     mfma_priority();
+    constexpr int NPV = C::KBLK * 2 * C::DBLK, NQK = C::DSTEPS * C::KBLK;
     if (G == 0) {
       load_v(t, PAR);
-      __builtin_amdgcn_sched_barrier(0);
+      load_k(t + 1, PAR ^ 1);
+      if (MASKED || FIRST) __builtin_amdgcn_sched_barrier(0);
     }
-    constexpr int NPV = C::KBLK * 2 * C::DBLK, NQK = C::DSTEPS * C::KBLK;
     if (MASKED) {
       // boundary tiles: a tile none of whose keys this wave's rows see adds exact
       // zeros to O and l, so its products and softmax are skipped (loads and
@@ -414,18 +432,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
       if (!FIRST) {
         pv(PAR ^ 1);
         qk(PAR);
-        schedule_mfma_phase_pv<NPV, NQK>();
+        schedule_mfma_phase_pv<NPV, NQK, G == 0 ? 2 * C::KDMA : 0>();
       } else {
         qk(PAR);
         schedule_mfma_phase<NQK>();
       }
     }
-    if (G == 1) wait_vm0();   // K(t+1) has landed: it is read after the barrier
     phase_barrier();
     valu_priority();
-    if (G == 1 && t + 2 < n_tiles) load_k(t + 2, PAR);
     if (!MASKED || !wave_blind(t)) softmax(t, mask_tag);
-    if (G == 0) wait_vm0();   // V(t) has landed: it is read after the barrier
+    if (G == 0) wait_vm0();   // V(t), K(t+1) have landed: they are read after the barrier
     phase_barrier();
   };
 
@@ -436,16 +452,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
     constexpr int G = decltype(grp_tag)::value;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // prologue: K(0) in LDS (V(0) is requested in the first period)
-    if (n_tiles > 0 && G == 1) load_k(0, 0);
-    if (G == 1) wait_vm0();
+    // prologue: K(0) in LDS (V(0) and K(1) are requested in the first period)
+    if (n_tiles > 0 && G == 0) load_k(0, 0);
+    wait_vm0();   // (and the Q fragments)
     phase_barrier();
     if (n_tiles > 0) {
-      if (G == 1) {
-        // G1 starts one phase late; meanwhile it requests K(1)
-        if (n_tiles > 1) load_k(1, 1);
-        phase_barrier();
-      }
+      if (G == 1) phase_barrier();   // G1 starts one phase late
       using T_ = std::true_type;
       using F_ = std::false_type;
       period(0, grp_tag, I0{}, T_{}, T_{});
