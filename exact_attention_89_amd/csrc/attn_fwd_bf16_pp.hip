@@ -154,7 +154,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   // wave-uniform values live in scalar registers, so branches on them are real
   // branches (a barrier must never sit in a lane-masked region)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;     // 0: G0 (stages V), 1: G1 (moves K)
+  const int grp = wave >> 2;     // 0: G0 (moves K and V), 1: G1
   const int wg = wave & 3;       // wave inside its group
   const int lane = tid & 63;
   const int lq = lane & 31;      // query column inside the wave's 32 rows
