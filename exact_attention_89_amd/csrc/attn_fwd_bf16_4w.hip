@@ -50,29 +50,10 @@
 
 #include "attn_bf16_tiles.hpp"
 #include "launch.hpp"
+#include "mfma_schedule.hpp"
 
 namespace attn89 {
 namespace {
-
-// Issue order of NM MFMAs with R fragment reads each: the reads of the first kPf MFMAs
-// first, then the reads of one more MFMA after every MFMA, so each fragment is requested
-// kPf MFMAs before it is used; NVM global requests (the next tile's DMA) go between the
-// MFMAs, as evenly as they fit.  Left to itself the compiler issues each read just
-// before its MFMA and the requests in one burst.
-template <int NM, int R, int NVM>
-__device__ __forceinline__ void schedule_mfma_run() {
-  constexpr int kPf = NM < 4 ? NM : 4;
-  constexpr int ITER = NM - kPf;
-  constexpr int VMI = ITER > 0 ? (NVM + ITER - 1) / ITER : 0;
-  __builtin_amdgcn_sched_group_barrier(0x100, R * kPf, 0);
-#pragma unroll
-  for (int i = 0; i < ITER; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-    if (VMI > 0 && i * VMI < NVM) __builtin_amdgcn_sched_group_barrier(0x020, VMI, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, kPf, 0);
-}
 
 template <int D, int RW = 4>
 struct Cfg {
@@ -341,7 +322,7 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     // b) scores; c) mask
     f32x16 scur[C::KBLK];
     qk(PAR, scur);
-    schedule_mfma_run<C::DSTEPS * C::KBLK, 1, LAST ? 0 : 2 * C::DMA>();
+    schedule_mfma_run<C::DSTEPS * C::KBLK, 1, LAST ? 0 : 2 * C::DMA, 4>();
     if (MASKED && needs_mask(t)) apply_mask(t, scur);
     // d) row maximum (in-lane, then with the partner lane) and the new reference;
     //    guard: a row with no valid key so far keeps m = -inf and uses 0 as its
@@ -398,7 +379,7 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
           const bf16x8 va = join_tr16(lds_tr16(vb), lds_tr16(vb + 4 * C::ROWB));
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kb][j], oacc[d], 0, 0, 0);
         }
-    schedule_mfma_run<C::KBLK * 2 * C::DBLK, 2, 0>();
+    schedule_mfma_run<C::KBLK * 2 * C::DBLK, 2, 0, 4>();
     // g) the next tile must be in LDS before any wave goes on (with key groups the
     //    caller holds the barrier, met by every group)
     if (!LAST && KS == 1) {

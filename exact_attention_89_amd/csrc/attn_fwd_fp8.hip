@@ -45,6 +45,7 @@
 
 #include "attn_fp8_tiles.hpp"
 #include "launch.hpp"
+#include "mfma_schedule.hpp"
 
 namespace attn89 {
 namespace {
@@ -221,6 +222,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
     }
     f32x16 scur[2];
     qk(PAR, scur);
+    schedule_mfma_run<C::DSTEPS * 2, 2, LAST ? 0 : 2 * C::DMA, 2>();
     if (MASKED && needs_mask(t)) apply_mask(t, scur);
     // row maximum and exponent reference (guard: a row without a valid key so far
     // keeps m = -inf and uses 0 as its reference)
@@ -262,6 +264,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdArgs p, float v
                                 lds_tr8(base + 32 * C::ROWB), lds_tr8(base + 48 * C::ROWB));
       oacc[d] = mfma_fp8(va, pf, oacc[d]);
     }
+    schedule_mfma_run<C::DBLK, 4, 0, 2>();
     if (!LAST) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's K(t+1), V(t+1) landed
       __syncthreads();

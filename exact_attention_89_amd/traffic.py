@@ -56,7 +56,7 @@ def _hash(files):
 def _kernel_hash():
     """Sources of the bf16 fused attention kernels."""
     return _hash(("attn_fwd_bf16_pp.hip", "attn_fwd_bf16_4w.hip", "attn_bf16_tiles.hpp",
-                  "common.hpp"))
+                  "common.hpp", "mfma_schedule.hpp"))
 
 
 def _headline_hash():
@@ -67,13 +67,13 @@ def _headline_hash():
 def _decode_hash():
     """Sources of the split-key decode path (the 4-wave kernel plus the merge)."""
     return _hash(("attn_fwd_bf16_4w.hip", "attn_bf16_tiles.hpp", "common.hpp",
-                  "attn_splitkv.hip"))
+                  "attn_splitkv.hip", "mfma_schedule.hpp"))
 
 
 def _fp8_hash():
     """Sources of the FP8 fused forward kernels."""
     return _hash(("attn_fwd_fp8.hip", "attn_fwd_fp8_pp.hip", "attn_fp8_tiles.hpp",
-                  "attn_bf16_tiles.hpp", "common.hpp"))
+                  "attn_bf16_tiles.hpp", "common.hpp", "mfma_schedule.hpp"))
 
 
 def _softmax_hash():
