@@ -45,13 +45,13 @@
 // them at the end of its softmax phase, before the barrier that publishes them.  (A
 // wave whose request the memory pipeline cannot take yet stalls; in a matrix phase
 // the matrix core works through its queued MFMAs meanwhile, in a softmax phase the
-// exponentials would wait.)  The 16-byte
-// chunks of a row are XOR-swizzled with a function of the row (kswz for K, vswz for
-// V), so the fragment reads are bank-conflict free: K fragments by ds_read_b128, the
-// P.V operand (8 consecutive keys of one dimension) by two transposing
-// ds_read_b64_tr_b16.  Buffer indices are compile-time constants (the loop is
-// unrolled by two), so every fragment address is a per-lane register computed once
-// plus an immediate offset.
+// exponentials would wait.)  The 16-byte chunks of a row are XOR-swizzled with a
+// function of the row (kswz for K, vswz for V), so the fragment reads are bank-conflict
+// free: K fragments by ds_read_b128, the P.V operand (8 consecutive keys of one
+// dimension) by two transposing ds_read_b64_tr_b16.  Each buffer is an LDS array of
+// its own (see the declarations below).  Buffer indices are compile-time constants
+// (the loop is unrolled by two), so every fragment address is a per-lane register
+// computed once plus an immediate offset.
 
 #include <type_traits>
 
