@@ -35,12 +35,17 @@ constexpr int kMaxResident = 16384;   // entries per row kept in registers
 __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
-// stores past the end of the resource are dropped
+// Stores past the end of the resource are dropped.  They are non-temporal (cache
+// policy bit 1, `nt`): every output element is written once and read by nobody in
+// the same launch, and streaming the writes past the caches instead of allocating
+// lines for them moved 8192 x 8192 from 99 to 77 us (1024 x 65536: 153 to 115 us).
+// Loads keep the default policy (non-temporal loads were slower).
+constexpr int kStoreNT = 2;
 __device__ __forceinline__ void store_f32(float v, __amdgpu_buffer_rsrc_t r, unsigned off) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, kStoreNT);
 }
 __device__ __forceinline__ void store_f32x4(f32x4 v, __amdgpu_buffer_rsrc_t r, unsigned off) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kStoreNT);
 }
 
 // VEC consecutive floats of a row from element index i (i % VEC == 0); entries at or
