@@ -1,8 +1,9 @@
 """Calls captured in a HIP graph (torch.cuda.CUDAGraph over the library's launches on the
 capturing stream) and replayed: every replay, with new inputs copied in between by
 ordinary eager work, must give bit for bit what the eager call gives on the same inputs.
-The no-allocation split-key entry point exists for such callers; attn_fwd and the
-allocating split-key entry point (with a workspace made before capture) are covered too.
+The no-allocation split-key entry point exists for such callers; attn_fwd, the
+allocating split-key entry point (with a workspace made before capture), the FP8 and
+variable-length entry points and the row softmax are covered too.
 Nothing is allocated inside a capture: outputs, workspaces and inputs are made first."""
 
 import math
@@ -13,7 +14,7 @@ import pytest
 
 import oracle
 from exact_attention_89_amd import api
-from exact_attention_89_amd.workloads import random_case
+from exact_attention_89_amd.workloads import random_case, random_fp8_case
 from tests.parity import check
 
 torch = pytest.importorskip("torch")
@@ -117,3 +118,93 @@ def test_attn_fwd_replays(B, H, N, D, causal, lens):
         api.attn_fwd(q, k, v, scale=scale, causal=causal, kv_lens=kvl, out=o, lse=l)
     _run_captured("attn_fwd", B, H, N, N, D, causal, lens, call,
                   with_oracle_first=(B * H * N <= 2 * 4 * 333))
+
+
+def _capture_and_replay(name, refill, call, outs):
+    """Capture call() (which writes the tensors in `outs`), then for each replay refill
+    the inputs eagerly, replay, and compare every output bit for bit with the same call
+    made eagerly on the same inputs."""
+    _say(f"[graph] {name}")
+    refill(900)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        refill(901 + r)
+        for t in outs:
+            t.fill_(float("nan") if t.is_floating_point() else 0)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        call()
+        torch.cuda.synchronize()
+        _say(f"[graph]   replay {r}")
+        for a, b in zip(got, outs):
+            assert torch.equal(a, b), f"{name}: replay {r} differs from the eager call"
+            assert not torch.isnan(a.float()).any(), f"{name}: replay {r} left NaN"
+
+
+def test_fp8_replays():
+    B, H, N, D = 2, 4, 300, 128
+    dev = "cuda"
+    q, k, v = (torch.empty((B, H, N, D), dtype=torch.uint8, device=dev) for _ in range(3))
+    kvl = torch.tensor([300, 170], dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def refill(seed):
+        # fresh E4M3 codes; the descale factors are kernel arguments, fixed at capture
+        for t, x in zip((q, k, v), random_fp8_case(seed, B, H, N, N, D)[:3]):
+            t.copy_(torch.from_numpy(np.ascontiguousarray(x)))
+
+    def call():
+        api.attn_fwd_fp8(q, k, v, 0.02, 0.03, 0.01, causal=True, kv_lens=kvl, out=o, lse=l)
+    _capture_and_replay("attn_fwd_fp8 B=2 H=4 N=300 D=128 causal, key lengths", refill, call,
+                        [o, l])
+
+
+def test_varlen_replays():
+    H, D = 4, 64
+    lens_q, lens_k = [70, 1, 200], [90, 130, 200]
+    dev = "cuda"
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32), device=dev)
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32), device=dev)
+    q = torch.empty((sum(lens_q), H, D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((sum(lens_k), H, D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    l = torch.empty((H, sum(lens_q)), dtype=torch.float32, device=dev)
+
+    def refill(seed):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        for t in (q, k, v):
+            t.copy_(torch.randn(t.shape, device=dev, generator=g).to(torch.bfloat16))
+
+    def call():
+        api.attn_fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q=max(lens_q),
+                            max_seqlen_k=max(lens_k), causal=True, out=o, lse=l)
+    _capture_and_replay("attn_fwd_varlen H=4 D=64 causal, 3 sequences", refill, call, [o, l])
+
+
+@pytest.mark.parametrize("rows,cols", [(300, 1000), (4, 70000)])
+def test_softmax_rows_replays(rows, cols):
+    dev = "cuda"
+    x = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+
+    def refill(seed):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        x.copy_(torch.randn(x.shape, device=dev, generator=g) * 4)
+
+    def call():
+        api.softmax_rows(x, out=y)
+    _capture_and_replay(f"softmax_rows {rows}x{cols}", refill, call, [y])
