@@ -47,6 +47,10 @@ __device__ __forceinline__ T lds_load(const lds_u8* base, unsigned off) {
 // is the same; when the reference moves both are multiplied by
 // alpha = exp2(m_old - m_new), the correction of the recurrence.
 constexpr float kRescaleSlack = 8.0f;
+// 2^(kRescaleSlack - 1): an exponential taken against a reference that has to move is
+// above this.  A lane whose exponentials of a tile sum to no more than this has none
+// that large, so a kernel may skip the row maxima of that tile.
+constexpr float kMoveSum = 128.0f;
 
 // K chunk swizzle: the 16 lanes served together read one chunk column of 16
 // consecutive rows; a 128-dimension row spans all 64 banks, a 64-dimension row half.

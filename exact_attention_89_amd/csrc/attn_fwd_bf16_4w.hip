@@ -305,6 +305,8 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
   float m_run = kNegInf;  // running maximum that set the reference (log2 domain)
   float m_use = 0.f;      // exponent reference: m_run, or 0 while m_run = -inf
   float m_thr = kNegInf;  // (m_run + kRescaleSlack) / c_exp: raw score that moves it
+  float e_thr = -1.f;     // lane sum of exponentials that calls for the maxima
+                          // (kMoveSum; -1, so every tile, while m_run = -inf)
   float l_run = 0.f;      // this lane's part of the running sum
   const float c_exp = p.c_exp;
 
@@ -324,49 +326,61 @@ void attn_fwd_bf16_4w_kernel(FwdArgs p) {
     qk(PAR, scur);
     schedule_mfma_run<C::DSTEPS * C::KBLK, 1, LAST ? 0 : 2 * C::DMA, 4>();
     if (MASKED && needs_mask(t)) apply_mask(t, scur);
-    // d) row maximum (in-lane, then with the partner lane) and the new reference;
-    //    guard: a row with no valid key so far keeps m = -inf and uses 0 as its
-    //    exponent reference, so no -inf - (-inf) is ever formed
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
-    mx = max_with_partner(mx);
-    // compared in the raw score domain, so the common case (no move) is one compare
-    const bool move = mx > m_thr;
-    if (__builtin_expect(__any(move), 0)) {
-      const float m_new = move ? mx * c_exp : m_run;
-      const float mu = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mu) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < C::DBLK; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-      m_run = m_new;
-      m_use = mu;
-      m_thr = (m_run + kRescaleSlack) / c_exp;
-    }
-    // e) P = exp2(s*c - m), rounded to bf16 in the B-operand layout of O^T = V^T P^T
+    // d) P = exp2(s*c - m) against the current exponent reference, rounded to bf16 in
+    //    the B-operand layout of O^T = V^T P^T; lsum = this lane's sum of the exponentials
     bf16x8 pf[C::KBLK][2];
-    float lsum = 0.f;
+    auto exps = [&]() {
+      float lsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < C::KBLK; ++kb)
+      for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 w;
+        for (int j = 0; j < 2; ++j) {
+          u32x4 w;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float e0 =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * j + 2 * x], c_exp, -m_use));
-          const float e1 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(scur[kb][8 * j + 2 * x + 1], c_exp, -m_use));
-          lsum += e0 + e1;
-          w[x] = pack_bf16x2(e0, e1);
+          for (int x = 0; x < 4; ++x) {
+            const float e0 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(scur[kb][8 * j + 2 * x], c_exp, -m_use));
+            const float e1 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(scur[kb][8 * j + 2 * x + 1], c_exp, -m_use));
+            lsum += e0 + e1;
+            w[x] = pack_bf16x2(e0, e1);
+          }
+          pf[kb][j] = __builtin_bit_cast(bf16x8, w);
         }
-        pf[kb][j] = __builtin_bit_cast(bf16x8, w);
+      return lsum;
+    };
+    float lsum = exps();
+    // e) a score above the move threshold m_thr has an exponential above e_thr, and so
+    //    has its lane's sum (every term >= 0): only when some lane's sum exceeds e_thr
+    //    are the row maxima (in-lane, then with the partner lane) formed and the
+    //    reference tested; below it none would move.  Guard: a row with no valid key
+    //    so far keeps m = -inf and uses 0 as its exponent reference, so no
+    //    -inf - (-inf) is ever formed.
+    if (__builtin_expect(__any(lsum > e_thr), 0)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
+      mx = max_with_partner(mx);
+      // compared in the raw score domain
+      const bool move = mx > m_thr;
+      if (__any(move)) {
+        const float m_new = move ? mx * c_exp : m_run;
+        const float mu = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mu) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+        m_run = m_new;
+        m_use = mu;
+        m_thr = (m_run + kRescaleSlack) / c_exp;
+        e_thr = m_run == kNegInf ? -1.f : kMoveSum;
+        lsum = exps();
       }
+    }
     l_run += lsum;
     // f) O^T += V^T P^T from V buffer PAR (P.V step 2kb + j covers keys 32kb + 16j ..)
 #pragma unroll

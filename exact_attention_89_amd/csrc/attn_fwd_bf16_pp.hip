@@ -279,6 +279,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
   float m_run = kNegInf;  // running maximum that set the reference (log2 domain)
   float m_use = 0.f;      // exponent reference: m_run, or 0 while m_run = -inf
   float m_thr = kNegInf;  // (m_run + kRescaleSlack) / c_exp: raw score that moves it
+  float e_thr = -1.f;     // lane sum of exponentials that calls for the maxima
+                          // (kMoveSum; -1, so every tile, while m_run = -inf)
   float l_run = 0.f;      // this lane's part of the running sum
   const float c_exp = p.c_exp;
 
@@ -308,46 +310,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
         }
   };
 
-  // softmax of tile t: mask, row maxima -> exponent reference, lazy correction of
-  // O and l, P = exp2(s*c - m) rounded to bf16 in the B-operand layout of P.V.
-  auto softmax = [&](int t, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(mask_tag)::value;
-    const int j0 = t * C::BC;
-    if (MASKED && (PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw))) {
-      // key j0 + off of this lane is visible iff off < lim (kv_len and causal bounds)
-      const int lim = min(L, p.causal ? qrow + 1 : L) - j0 - 8 * lg;
-#pragma unroll
-      for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = kb * 32 + 16 * (r >> 3) + (r & 7);
-          const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
-          sacc[kb][r] = off < lim ? x : kNegInf;
-        }
-    }
-    // guard: a row with no valid key so far keeps m = -inf and uses 0 as its
-    // exponent reference, so no -inf - (-inf) is ever formed
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = max_with_partner(mx);
-    // compared in the raw score domain, so the common case (no move) is one compare
-    const bool move = mx > m_thr;
-    if (__builtin_expect(__any(move), 0)) {
-      const float m_new = move ? mx * c_exp : m_run;
-      const float mu = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mu) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < C::DBLK; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-      m_run = m_new;
-      m_use = mu;
-      m_thr = (m_run + kRescaleSlack) / c_exp;
-    }
+  // P(t) = exp2(s*c - m) against the current exponent reference, rounded to bf16 in
+  // the B-operand layout of P.V; returns this lane's sum of the exponentials
+  auto exps = [&]() __attribute__((always_inline)) {
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
@@ -365,6 +330,60 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_pp_kernel(FwdArgs p) {
         }
         pf[kb][j] = __builtin_bit_cast(bf16x8, w);
       }
+    return lsum;
+  };
+
+  // softmax of tile t: mask, exponentials against the current reference, and only when
+  // some exponential may exceed 2^kRescaleSlack the row maxima, the lazy correction of
+  // O and l and the exponentials again.
+  auto softmax = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    const int j0 = t * C::BC;
+    if (MASKED && (PRE || (j0 + C::BC > L) || (p.causal && j0 + C::BC - 1 > qw))) {
+      // key j0 + off of this lane is visible iff off < lim (kv_len and causal bounds)
+      const int lim = min(L, p.causal ? qrow + 1 : L) - j0 - 8 * lg;
+#pragma unroll
+      for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 16 * (r >> 3) + (r & 7);
+          const float x = PRE ? sacc[kb][r] * p.c_pre : sacc[kb][r];
+          sacc[kb][r] = off < lim ? x : kNegInf;
+        }
+    }
+    float lsum = exps();
+    // A score above the move threshold m_thr has an exponential above e_thr (half of
+    // 2^kRescaleSlack, far more than the rounding of the two tests apart), and then so
+    // has the lane's sum, every term being >= 0.  So the maxima are needed only when some
+    // lane's sum exceeds e_thr; below it no reference of the wave moves, exactly as
+    // the test on the maxima would have found.
+    if (__builtin_expect(__any(lsum > e_thr), 0)) {
+      // guard: a row with no valid key so far keeps m = -inf and uses 0 as its
+      // exponent reference, so no -inf - (-inf) is ever formed
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = max_with_partner(mx);
+      // compared in the raw score domain
+      const bool move = mx > m_thr;
+      if (__any(move)) {
+        const float m_new = move ? mx * c_exp : m_run;
+        const float mu = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mu) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+        m_run = m_new;
+        m_use = mu;
+        m_thr = (m_run + kRescaleSlack) / c_exp;
+        e_thr = m_run == kNegInf ? -1.f : kMoveSum;
+        lsum = exps();
+      }
+    }
     l_run += lsum;
   };
 
