@@ -148,6 +148,38 @@ def test_fused_bf16_rising_max(bf16_kernel):
     check(o, lse, o_ref, lse_ref, "bf16", "rising max")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fused_bf16_reference_moves(D, causal, bf16_kernel):
+    """Scores placed exactly (one-hot Q, key weights on the same axis, all integers, so
+    s * scale * log2(e) is about the weight in log2 units) to drive each branch of the
+    lazy exponent reference: keys 64.. at +6 over the first tile (every exponential
+    about 2^6: lane sums far above 2^7 but no reference moves), one key at +13 at
+    position 777 (a move caused by one key), keys 1000..1063 at +21 (a move of whole
+    rows late in the sequence) and a negative plateau after them."""
+    rng = np.random.default_rng(31 + D)
+    Nq = Nk = 1100                                # causal rows reach every key
+    from exact_attention_89_amd.workloads import round_to_bf16
+    c = math.log2(math.e) / math.sqrt(D)
+    alpha = 8.0                                   # exact in bf16
+    w = np.zeros(Nk, np.float32)
+    w[64:] = 6.0
+    w[777] = 13.0
+    w[1000:1064] = 21.0
+    w[1064:] = -4.0
+    beta = np.round(w / (alpha * c)).astype(np.float32)   # integers, exact in bf16
+    q = np.zeros((1, 2, Nq, D), np.float32)
+    q[..., 0] = alpha
+    k = round_to_bf16(np.float32(0.05) * rng.standard_normal((1, 2, Nk, D), dtype=np.float32))
+    k[..., 0] = beta
+    v = round_to_bf16(rng.standard_normal((1, 2, Nk, D), dtype=np.float32))
+    scale = 1 / math.sqrt(D)
+    _say(f"[parity] fused bf16 reference moves D={D} causal={causal}")
+    o, lse = _run("fused", q, k, v, scale, causal, None, "bf16")
+    o_ref, lse_ref = oracle.attention_oracle(q, k, v, scale, causal=causal)
+    check(o, lse, o_ref, lse_ref, "bf16", "reference moves")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (False, [0, 77]),
                                          (True, [130, 2])])
