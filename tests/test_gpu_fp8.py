@@ -90,6 +90,32 @@ def test_fp8_kv_lens(causal, lens, D, fp8_kernel):
     _run(4, 2, 700, 700, D, causal, lens=lens, seed=11 + D)
 
 
+@pytest.mark.parametrize("B,H,N,D,causal,lens", [
+    (1, 16, 1024, 128, True, None),           # B*H = 16, causal: heads two at a time per XCD
+    (2, 16, 600, 64, True, [600, 377]),       # B*H = 32, ragged query blocks and key lengths
+    (1, 24, 520, 128, True, None),            # B*H = 24: a multiple of 8 but not of 16
+])
+def test_fp8_schedules(B, H, N, D, causal, lens, fp8_kernel):
+    """Each (batch, head, query block) is computed once whichever order the workgroups
+    take them in: O and LSE start as NaN and every element is checked against the
+    oracle's bound."""
+    q8, k8, v8, ds = random_fp8_case(B * 1000 + H + N, B, H, N, N, D)
+    scale = 1.0 / math.sqrt(D)
+    _say(f"[fp8] schedules B={B} H={H} N={N} D={D} causal={causal} lens={lens}")
+    ld = None if lens is None else torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    o = torch.full((B, H, N, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    api.attn_fwd_fp8(_dev(q8), _dev(k8), _dev(v8), *ds, scale=scale, causal=causal,
+                     kv_lens=ld, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref, P = oracle.attention_fp8_oracle(q8, k8, v8, scale, *ds, causal=causal,
+                                                    kv_lens=lens, return_probs=True)
+    sa = fp8_score_abs(oracle.dequantize(q8, ds[0]), oracle.dequantize(k8, ds[1]), scale)
+    bound = fp8_o_bound(P, oracle.dequantize(v8, ds[2]), o_ref, sa)
+    check_fp8(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, bound,
+              f"fp8 schedules {B}x{H}x{N}x{D}")
+
+
 @pytest.mark.parametrize("std", [0.25, 2.0, 4.0])
 def test_fp8_peaked_and_flat_rows(std, fp8_kernel):
     """Larger std gives peaked rows (one key dominates), smaller nearly uniform rows."""

@@ -148,6 +148,28 @@ def test_fused_bf16_rising_max(bf16_kernel):
     check(o, lse, o_ref, lse_ref, "bf16", "rising max")
 
 
+@pytest.mark.parametrize("B,H,N,D,causal,lens", [
+    (1, 16, 1024, 64, True, None),            # B*H = 16, causal: heads two at a time per XCD
+    (2, 16, 600, 128, True, [600, 377]),      # B*H = 32, ragged query blocks and key lengths
+    (1, 24, 520, 128, True, None),            # B*H = 24: a multiple of 8 but not of 16
+    (3, 8, 700, 64, False, [700, 1, 450]),    # non-causal: heads one at a time per XCD
+])
+def test_fused_bf16_schedules(B, H, N, D, causal, lens, bf16_kernel):
+    """Each (batch, head, query block) is computed once whichever order the workgroups
+    take them in: O and LSE start as NaN and every element is compared with the oracle."""
+    q, k, v, lens = random_case(B * 1000 + H + N, B, H, N, N, D, "bf16", lens)
+    scale = 1.0 / math.sqrt(D)
+    _say(f"[parity] schedules B={B} H={H} N={N} D={D} causal={causal} lens={lens}")
+    o = torch.full((B, H, N, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    api.attn_fwd(_dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16"), scale=scale, causal=causal,
+                 kv_lens=_lens_dev(lens), out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_oracle(q, k, v, scale, causal=causal, kv_lens=lens)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "bf16",
+          what=f"schedules {B}x{H}x{N}x{D}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
 def test_fused_bf16_reference_moves(D, causal, bf16_kernel):
