@@ -132,16 +132,36 @@ def _prep(q, k, v, kv_lens, dtype):
     return torch, q, k, v, kv_lens, (B, H, Nq, k.shape[2], D)
 
 
+def _outputs(torch, q, out, lse, dtype, lse_shape):
+    """Allocate O (like q, of `dtype`) and the LSE, or check the caller's: the kernels
+    write every element, so a wrong shape, type or layout would write out of bounds."""
+    o = torch.empty(q.shape, dtype=dtype, device=q.device) if out is None else out
+    l = torch.empty(lse_shape, dtype=torch.float32, device=q.device) if lse is None else lse
+    if (not isinstance(o, torch.Tensor) or o.shape != q.shape or o.dtype != dtype
+            or not o.is_contiguous() or o.device != q.device):
+        raise ValueError(f"out must be a contiguous {dtype} tensor shaped like q on q's device")
+    if (not isinstance(l, torch.Tensor) or tuple(l.shape) != tuple(lse_shape)
+            or l.dtype != torch.float32 or not l.is_contiguous() or l.device != q.device):
+        raise ValueError(f"lse must be a contiguous float32 {list(lse_shape)} tensor on q's "
+                         "device")
+    return o, l
+
+
+def _workspace(torch, q, workspace, need):
+    """Allocate the workspace, or check the caller's (the library checks its size)."""
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=q.device)
+    if (not isinstance(workspace, torch.Tensor) or workspace.device != q.device
+            or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    return workspace
+
+
 def _call_fwd(fname, q, k, v, scale, causal, kv_lens, out, lse, dtype):
     torch, q, k, v, kv_lens, (B, H, Nq, Nk, D) = _prep(q, k, v, kv_lens, dtype)
     if scale is None:
         scale = D ** -0.5
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    if o.shape != q.shape or o.dtype != dtype or not o.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    if l.shape != (B, H, Nq) or l.dtype != torch.float32 or not l.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    o, l = _outputs(torch, q, out, lse, dtype, (B, H, Nq))
     lib = load_library()
     st = getattr(lib, fname)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                              l.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
@@ -264,11 +284,9 @@ def attn_materialized(q, k, v, scale: Optional[float] = None, causal: bool = Fal
     if scale is None:
         scale = D ** -0.5
     lib = load_library()
-    need = int(lib.attn_materialized_workspace_bytes(B, H, Nq, Nk))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = 0 if workspace is not None else int(lib.attn_materialized_workspace_bytes(B, H, Nq, Nk))
+    workspace = _workspace(torch, q, workspace, need)
+    o, l = _outputs(torch, q, out, lse, torch_bf16(), (B, H, Nq))
     st = lib.attn_materialized(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                l.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
                                kv_lens.data_ptr() if kv_lens is not None else None,
@@ -330,11 +348,9 @@ def attn_partial(q, k, v, scale: Optional[float] = None, causal: bool = False,
     if scale is None:
         scale = D ** -0.5
     lib = load_library()
-    need = int(lib.attn_partial_workspace_bytes(B, H, Nq, Nk))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = 0 if workspace is not None else int(lib.attn_partial_workspace_bytes(B, H, Nq, Nk))
+    workspace = _workspace(torch, q, workspace, need)
+    o, l = _outputs(torch, q, out, lse, torch_bf16(), (B, H, Nq))
     st = lib.attn_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                           l.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
                           kv_lens.data_ptr() if kv_lens is not None else None,
@@ -356,11 +372,10 @@ def attn_fwd_splitkv(q, k, v, scale: Optional[float] = None, causal: bool = Fals
     if scale is None:
         scale = D ** -0.5
     lib = load_library()
-    need = int(lib.attn_splitkv_workspace_bytes(B, H, Nq, Nk, D, int(num_splits)))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = 0 if workspace is not None else int(
+        lib.attn_splitkv_workspace_bytes(B, H, Nq, Nk, D, int(num_splits)))
+    workspace = _workspace(torch, q, workspace, need)
+    o, l = _outputs(torch, q, out, lse, torch_bf16(), (B, H, Nq))
     st = lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                               l.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
                               kv_lens.data_ptr() if kv_lens is not None else None,
@@ -382,8 +397,7 @@ def attn_fwd_splitkv_noalloc(q, k, v, scale: Optional[float] = None, causal: boo
     torch, q, k, v, kv_lens, (B, H, Nq, Nk, D) = _prep(q, k, v, kv_lens, torch_bf16())
     if scale is None:
         scale = D ** -0.5
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, l = _outputs(torch, q, out, lse, torch_bf16(), (B, H, Nq))
     st = load_library().attn_fwd_splitkv_noalloc(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Nq, Nk, D,
         float(scale), int(bool(causal)), kv_lens.data_ptr() if kv_lens is not None else None,
